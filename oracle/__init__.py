@@ -1,0 +1,158 @@
+"""Oracle: plain fp64 CPU scaled-dot-product attention. TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library never imports it and
+shares no code with it.
+
+The arithmetic lives in ``oracle.cpp`` (see its header for the sources on the
+pages and the readings taken). This module only marshals numpy float64
+arrays into that library through ctypes and builds it with g++ when it is
+missing.
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to something
+other than itself: torch's CPU attention in float64 (the pages' own check),
+closed forms, invariants, finite differences and a hand-worked golden case.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.cpp into liboracle.so with g++ (IEEE math, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        D = ctypes.c_double
+        I = ctypes.c_int
+        lib.oracle_hardware_threads.restype = I
+        lib.oracle_attn_rows.argtypes = [P, P, I64, P, P, I64, I64, D, I, P, P, I]
+        lib.oracle_fwd.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I, P, P, I]
+        lib.oracle_fwd_varlen.argtypes = [P, P, P, P, P, I64, I64, I64, D, I, P, P, I]
+        lib.oracle_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, I, P, P, P, P, P, I]
+        lib.oracle_bwd_varlen.argtypes = [P, P, P, P, P, P, I64, I64, I64, D, I, P, P, P, P, P, I]
+        for f in ("oracle_attn_rows", "oracle_fwd", "oracle_fwd_varlen", "oracle_bwd",
+                  "oracle_bwd_varlen"):
+            getattr(lib, f).restype = None
+        _lib = lib
+    return _lib
+
+
+def hardware_threads() -> int:
+    return int(_load().oracle_hardware_threads())
+
+
+def _f64(a) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    return a
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(q, k, v, scale: float, causal: bool, threads: int = 0):
+    """Dense forward. q [b,h,s_q,d], k/v [b,h,s_kv,d] -> (o [b,h,s_q,d], lse [b,h,s_q])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, h, s_q, d = q.shape
+    s_kv = k.shape[2]
+    assert k.shape == (b, h, s_kv, d) and v.shape == (b, h, s_kv, d)
+    o = np.zeros((b, h, s_q, d))
+    lse = np.zeros((b, h, s_q))
+    _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), b, h, s_q, s_kv, d, float(scale),
+                       int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    return o, lse
+
+
+def attn_rows(q_rows, q_pos, k, v, scale: float, causal: bool, threads: int = 0):
+    """Selected rows of one head. q_rows [n,d] at positions q_pos [n]; k/v [s_kv,d]."""
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    pos = np.ascontiguousarray(np.asarray(q_pos, dtype=np.int64))
+    n, d = q_rows.shape
+    s_kv = k.shape[0]
+    assert pos.shape == (n,) and k.shape == (s_kv, d) and v.shape == (s_kv, d)
+    o = np.zeros((n, d))
+    lse = np.zeros((n,))
+    _load().oracle_attn_rows(_ptr(q_rows), _ptr(pos), n, _ptr(k), _ptr(v), s_kv, d,
+                             float(scale), int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0):
+    """Packed THD forward. q [T_q,h,d], k/v [T_kv,h,d], cu_* [n+1] -> (o [T_q,h,d], lse [T_q,h])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu_q, cu_kv = _i32(cu_q), _i32(cu_kv)
+    n = cu_q.shape[0] - 1
+    t_q, h, d = q.shape
+    assert cu_kv.shape == cu_q.shape and cu_q[-1] <= t_q and cu_kv[-1] <= k.shape[0]
+    o = np.zeros((t_q, h, d))
+    lse = np.zeros((t_q, h))
+    _load().oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_kv), n, h, d,
+                              float(scale), int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    return o, lse
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
+    """Dense backward with the oracle's own forward.
+
+    Returns (o, lse, dq, dk, dv), all float64, BHSD / [b,h,s_q].
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    b, h, s_q, d = q.shape
+    s_kv = k.shape[2]
+    assert dout.shape == q.shape and k.shape == v.shape == (b, h, s_kv, d)
+    o = np.zeros_like(q)
+    lse = np.zeros((b, h, s_q))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), b, h, s_q, s_kv, d, float(scale),
+                       int(bool(causal)), _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                       int(threads))
+    return o, lse, dq, dk, dv
+
+
+def bwd_varlen(q, k, v, dout, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0):
+    """Packed THD backward with the oracle's own forward. Returns (o, lse, dq, dk, dv)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu_q, cu_kv = _i32(cu_q), _i32(cu_kv)
+    n = cu_q.shape[0] - 1
+    t_q, h, d = q.shape
+    o = np.zeros_like(q)
+    lse = np.zeros((t_q, h))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    _load().oracle_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_q), _ptr(cu_kv), n,
+                              h, d, float(scale), int(bool(causal)), _ptr(o), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), int(threads))
+    return o, lse, dq, dk, dv
