@@ -1,0 +1,144 @@
+/*
+ * sdpa.h -- C ABI of libsdpa07: fused scaled-dot-product attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (the plain definition; the pages name it without a formula):
+ *   O = softmax(scale * Q K^T + mask) V,  LSE_i = ln sum_{j visible} exp(scale q_i . k_j)
+ * "Inside NVIDIA's cuDNN Graph API: Fusion, Autotuning, and Plan Reuse with
+ * cuDNN Frontend", section 5 "SDPA (Flash Attention) with causal masking":
+ * Q, K, V of logical shape (b, h, s, d), an attention scale, and causal
+ * masking as a top-left diagonal band with right bound 0, i.e. query i sees
+ * key j iff j <= i (also when s_q != s_kv).
+ * cudnn-frontend PR #554 "torch: put torch.sdpa on the cuDNN Python API
+ * (CUDNN provider + dense backward)": the forward's optional per-row
+ * statistic (aten's logsumexp: fp32, (b, h, s) dense, (T, h) token-major for
+ * packed THD); packed THD batches indexed by int32 cu_seqlens prefix sums with
+ * max_seqlen bounds and no attention across sequences; the dense backward
+ * producing dQ, dK, dV from Q, K, V, O, dO and the statistic; operands whose
+ * innermost dimension is dense and whose base is 16-byte aligned.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *    library allocates no device memory and keeps no pointer after return.
+ *  - Strides are in ELEMENTS. Dense tensors take 4 strides in logical
+ *    (b, h, s, d) order, packed THD tensors 3 strides in (t, h, d) order. The
+ *    d stride must be 1; every other stride, and every base pointer, must
+ *    keep 16-byte alignment of each row (multiples of 8 elements for
+ *    fp16/bf16, 4 for fp32). Any permutation of the outer dimensions works
+ *    (BHSD, BSHD, ...).
+ *  - One io dtype per call for Q, K, V, O (and dO, dQ, dK, dV); LSE is always
+ *    fp32. Accumulation is fp32.
+ *  - Head dims d in {64, 128}.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *    enqueues kernels on it and returns; nothing is synchronised and device
+ *    memory is never read by the host. Calls are thread-safe.
+ *  - A row with no visible key (s_kv = 0, or a packed sequence with no keys)
+ *    gets O = 0 and LSE = -inf. Sizes of zero return SDPA_OK without
+ *    launching.
+ *  - Errors: functions never throw. On a non-OK status, sdpa_last_error()
+ *    returns a message for the calling thread.
+ *      SDPA_ERR_INVALID_ARG  null required pointer, negative size, non-finite
+ *                            scale, bad workspace, int32 index overflow
+ *      SDPA_ERR_UNSUPPORTED  dtype, head dim, d stride != 1, misaligned base
+ *                            pointer or stride
+ *      SDPA_ERR_LAUNCH       the HIP runtime rejected a launch
+ */
+#ifndef SDPA07_SDPA_H
+#define SDPA07_SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID_ARG = 1,
+  SDPA_ERR_UNSUPPORTED = 2,
+  SDPA_ERR_LAUNCH = 3
+} sdpa_status;
+
+typedef enum { SDPA_FP32 = 0, SDPA_FP16 = 1, SDPA_BF16 = 2 } sdpa_dtype;
+
+/*
+ * Dense forward.
+ *   q: (b, h, s_q, d)   k, v: (b, h, s_kv, d)   o: (b, h, s_q, d), written
+ *   lse: fp32 (b, h, s_q) contiguous, written; may be NULL (not produced)
+ *   scale: multiplies Q K^T (pass 1/sqrt(d) for the usual scaling)
+ *   causal: 0 or 1 (top-left)
+ * Cited: the cuDNN Graph API article, section 5 (operation, scale, causal);
+ * cudnn-frontend PR #554 (statistic layout (B, H, S) fp32).
+ */
+sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     sdpa_dtype dtype, int b, int h, int s_q, int s_kv, int d,
+                     const int64_t q_stride[4], const int64_t k_stride[4],
+                     const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                     int causal, void* stream);
+
+/*
+ * Packed THD (varlen) forward.
+ *   q, o: (total_q, h, d); k, v: (total_kv, h, d); strides in (t, h, d) order.
+ *   cu_seqlens_q, cu_seqlens_kv: DEVICE int32 [num_seqs + 1], non-decreasing,
+ *     cu[0] = 0, cu[num_seqs] <= total. Sequence n owns tokens
+ *     [cu[n], cu[n+1]); positions (and the causal test) are local to it.
+ *   max_seqlen_q: an upper bound on every query length (sizes the grid);
+ *     max_seqlen_kv: an upper bound on every key length (checked only > 0).
+ *   lse: fp32 (total_q, h) token-major contiguous; may be NULL.
+ * The cu_seqlens contents are a caller contract (the host never reads them);
+ * the kernels clamp every row index to [0, total) so rows at or beyond
+ * total_q / total_kv (e.g. an allocation's capacity tail) are never read or
+ * written, and query rows beyond a sequence's length are never written.
+ * Cited: cudnn-frontend PR #554 (THD packing with cu_seqlens and max_seqlen,
+ * (T, H, 1) token-major statistic); its merge log, the FP8 d512 forward entry
+ * (keys past the packed total must not feed P.V; dead rows get -inf).
+ */
+sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                            int max_seqlen_kv, sdpa_dtype dtype, int h, int d,
+                            const int64_t q_stride[3], const int64_t k_stride[3],
+                            const int64_t v_stride[3], const int64_t o_stride[3], float scale,
+                            int causal, void* stream);
+
+/*
+ * Bytes of device workspace sdpa_bwd needs for these sizes (fp32 row
+ * statistics, 256-byte aligned). The caller allocates it.
+ */
+size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype);
+
+/*
+ * Dense backward (fp16/bf16).
+ *   q, k, v, o, dout as in sdpa_fwd (o is the forward's output, dout = dL/dO);
+ *   lse: fp32 (b, h, s_q) contiguous, the forward's statistic (required);
+ *   dq, dk, dv: written, same logical shapes as q, k, v, with their own
+ *     strides (e.g. the inputs' permutation);
+ *   workspace: device buffer of at least sdpa_bwd_workspace_size() bytes,
+ *     256-byte aligned; its contents on entry are ignored.
+ * Deterministic: no atomics; repeated calls give bit-identical gradients.
+ * Three kernels on `stream`: rowsum(dO * O), a dK/dV pass, a dQ pass.
+ * Cited: cudnn-frontend PR #554 (dense backward, gradients in the inputs'
+ * layouts, deterministic flag honoured); its merge log, the SM80 backward
+ * TemplateParams entry (the chain starts with the dO.O row dot product).
+ */
+sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
+                     int s_q, int s_kv, int d, const int64_t q_stride[4],
+                     const int64_t k_stride[4], const int64_t v_stride[4],
+                     const int64_t o_stride[4], const int64_t do_stride[4],
+                     const int64_t dq_stride[4], const int64_t dk_stride[4],
+                     const int64_t dv_stride[4], float scale, int causal, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* sdpa_last_error(void);
+
+/* Library version string. */
+const char* sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA07_SDPA_H */

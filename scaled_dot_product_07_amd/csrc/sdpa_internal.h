@@ -1,0 +1,76 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the HIP kernels.
+// Not installed; the public interface is include/sdpa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa07 {
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Forward launch parameters. Strides are in elements; the d stride is 1.
+// Dense: index (b, h, s). Packed THD: the "b" index is the sequence, the
+// b strides are unused and rows start at cu_seqlens[n].
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int b;          // batch (dense) or number of sequences (packed)
+  int h;
+  int s_q, s_kv;  // dense lengths (unused when packed)
+  int n_qtiles;   // query tiles per (b, h): ceil(s_q or max_seqlen_q / BM)
+  float scale_log2;  // |scale| * log2(e)
+  int negate_q;      // 1 when scale < 0 (the sign is moved onto Q, exactly)
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  int total_q, total_kv;
+};
+
+// Backward launch parameters (dense).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: rowsum(dO * O), fp32 [b][h][s_q]
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  int b, h, s_q, s_kv;
+  float scale;       // the signed attention scale
+  float scale_log2;  // scale * log2(e)
+};
+
+constexpr int kFwdBlockM = 128;  // query rows per workgroup (32 per wave)
+constexpr int kFwdBlockN = 64;   // keys per K/V tile
+constexpr int kFwdThreads = 256;
+
+// Enqueue the forward; returns the launch status.
+hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
+                      hipStream_t stream);
+
+// Enqueue the three backward kernels; returns the first failing launch status.
+hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream);
+
+// Query tiles of the dK/dV and dQ passes (exported for grid sizing).
+constexpr int kBwdBlockM = 64;
+constexpr int kBwdBlockN = 64;
+
+}  // namespace sdpa07

@@ -1,0 +1,163 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and every validation path returns its status and message before any HIP call.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FP32, FP16, BF16 = 0, 1, 2
+ALIGNED = 0x10000  # a fake 16-byte aligned device address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import scaled_dot_product_07_amd as sdpa
+    return sdpa._load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(sdpa_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("sdpa_fwd", "sdpa_fwd_varlen", "sdpa_bwd", "sdpa_bwd_workspace_size",
+              "sdpa_last_error", "sdpa_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), f"{s} not exported"
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.sdpa_version()
+
+
+def S4(*x):
+    return (ctypes.c_int64 * 4)(*x)
+
+
+def S3(*x):
+    return (ctypes.c_int64 * 3)(*x)
+
+
+def dense_st(b, h, s, d):
+    return S4(h * s * d, s * d, d, 1)
+
+
+def fwd(lib, q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=None, dt=BF16, b=1, h=1, sq=8,
+        skv=8, d=64, st=None, scale=0.125, causal=1):
+    qs = st or dense_st(b, h, sq, d)
+    ks = st or dense_st(b, h, skv, d)
+    return lib.sdpa_fwd(q, k, v, o, lse, dt, b, h, sq, skv, d, qs, ks, ks, qs, scale, causal,
+                        None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=7), UNSUPPORTED, "dtype"),
+    (dict(b=-1), INVALID, "negative"),
+    (dict(d=96), UNSUPPORTED, "head dim"),
+    (dict(d=32), UNSUPPORTED, "head dim"),
+    (dict(scale=math.inf), INVALID, "scale"),
+    (dict(scale=math.nan), INVALID, "scale"),
+    (dict(causal=2), INVALID, "causal"),
+    (dict(q=None), INVALID, "q: NULL"),
+    (dict(o=None), INVALID, "o: NULL"),
+    (dict(k=ALIGNED + 2), UNSUPPORTED, "16-byte"),
+    (dict(st=S4(64 * 8, 64 * 8, 64, 2)), UNSUPPORTED, "innermost"),
+    (dict(st=S4(64 * 8, 64 * 8, 68, 1)), UNSUPPORTED, "alignment"),
+    (dict(lse=ALIGNED + 1), UNSUPPORTED, "lse"),
+    (dict(b=100000, h=100000, sq=1000), INVALID, "int32"),
+])
+def test_fwd_validation(lib, kw, status, msg):
+    assert fwd(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+def test_fwd_zero_sizes_return_ok_without_launch(lib):
+    for kw in (dict(b=0), dict(h=0), dict(sq=0)):
+        assert fwd(lib, q=None, k=None, v=None, o=None, **kw) == OK
+        assert lib.sdpa_last_error() == b""
+
+
+def test_fwd_fp32_needs_4_element_strides(lib):
+    # fp32 rows of d=64 floats: a row stride of 68 floats keeps 16-byte alignment
+    assert fwd(lib, dt=FP32, b=1, h=1, sq=0, st=S4(0, 0, 68, 1)) == OK
+
+
+def varlen(lib, cu_q=ALIGNED, cu_kv=ALIGNED, n=2, tq=16, tkv=16, maxq=8, maxkv=8, dt=BF16, h=2,
+           d=64, st=None, scale=0.1, causal=1, q=ALIGNED):
+    s = st or S3(h * d, d, 1)
+    return lib.sdpa_fwd_varlen(q, ALIGNED, ALIGNED, ALIGNED, None, cu_q, cu_kv, n, tq, tkv, maxq,
+                               maxkv, dt, h, d, s, s, s, s, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(cu_q=None), INVALID, "cu_seqlens"),
+    (dict(cu_kv=None), INVALID, "cu_seqlens"),
+    (dict(maxq=0), INVALID, "max_seqlen"),
+    (dict(maxkv=0), INVALID, "max_seqlen"),
+    (dict(maxq=17), INVALID, "exceeds total_q"),
+    (dict(n=-1), INVALID, "negative"),
+    (dict(d=80), UNSUPPORTED, "head dim"),
+    (dict(st=S3(2 * 64, 64, 3)), UNSUPPORTED, "innermost"),
+    (dict(q=None), INVALID, "q: NULL"),
+])
+def test_varlen_validation(lib, kw, status, msg):
+    assert varlen(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+def test_varlen_empty_batch_ok(lib):
+    assert varlen(lib, cu_q=None, cu_kv=None, n=0) == OK
+    assert varlen(lib, tq=0, maxq=0) == OK
+
+
+def test_bwd_workspace_size(lib):
+    lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
+    n = lib.sdpa_bwd_workspace_size(4, 16, 2048, 128, BF16)
+    assert n >= 4 * 16 * 2048 * 4 and n % 256 == 0
+
+
+def bwd(lib, dt=BF16, lse=ALIGNED, ws=ALIGNED, ws_bytes=1 << 20, d=64, b=1, h=1, s=8,
+        causal=1, scale=0.1):
+    st = dense_st(b, h, s, d)
+    P = ALIGNED
+    return lib.sdpa_bwd(P, P, P, P, P, lse, P, P, P, ws, ws_bytes, dt, b, h, s, s, d,
+                        st, st, st, st, st, st, st, st, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=FP32), UNSUPPORTED, "fp16 and bf16"),
+    (dict(lse=None), INVALID, "lse"),
+    (dict(ws=None), INVALID, "workspace"),
+    (dict(ws=ALIGNED + 16), INVALID, "256-byte"),
+    (dict(ws_bytes=8), INVALID, "smaller"),
+    (dict(d=256), UNSUPPORTED, "head dim"),
+    (dict(scale=math.inf), INVALID, "scale"),
+])
+def test_bwd_validation(lib, kw, status, msg):
+    assert bwd(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+def test_python_binding_maps_statuses(lib):
+    import scaled_dot_product_07_amd as sdpa
+    assert sdpa._check(OK) is None
+    lib.sdpa_fwd(None, None, None, None, None, BF16, 1, 1, 8, 8, 96, dense_st(1, 1, 8, 96),
+                 dense_st(1, 1, 8, 96), dense_st(1, 1, 8, 96), dense_st(1, 1, 8, 96), 0.1, 0, None)
+    with pytest.raises(NotImplementedError):
+        sdpa._check(UNSUPPORTED)
+    with pytest.raises(ValueError):
+        sdpa._check(INVALID)

@@ -1,0 +1,104 @@
+"""GPU parity of the packed THD forward (sdpa_fwd_varlen) against the fp64 oracle.
+
+Every packed buffer is allocated with a NaN-poisoned capacity tail (rows past
+the packed total), and O / LSE tails are pre-filled with a sentinel: the
+kernels must neither read the poison (O stays finite and matches) nor write
+past the total (the sentinels survive).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import announce, check_lse, check_o, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, h, d, scale, causal, dev, max_q=None, max_kv=None):
+    import scaled_dot_product_07_amd as sdpa
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    cu_q, cu_kv = inp.cu_q.to(dev), inp.cu_kv.to(dev)
+    o = torch.full_like(q, 77.0)
+    lse = torch.full((q.shape[0], h), 55.0, dtype=torch.float32, device=dev)
+    max_q = int(inp.lens_q.max()) if max_q is None else max_q
+    max_kv = max(int(inp.lens_kv.max()), 1) if max_kv is None else max_kv
+    sdpa.fwd_varlen(q, k, v, cu_q, cu_kv, max_q, max_kv, total_q=inp.total_q,
+                    total_kv=inp.total_kv, scale=scale, causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_all(inp, o, lse, scale, causal, dt):
+    tq = inp.total_q
+    o_ref, lse_ref = oracle.fwd_varlen(f64(inp.q[:tq]), f64(inp.k[:inp.total_kv]),
+                                       f64(inp.v[:inp.total_kv]), inp.cu_q.numpy(),
+                                       inp.cu_kv.numpy(), scale, causal)
+    check_o(f64(o[:tq]), o_ref, dt)
+    check_lse(f64(lse[:tq]), lse_ref)
+    assert torch.all(o[tq:] == 77.0), "O written past the packed total"
+    assert torch.all(lse[tq:] == 55.0), "LSE written past the packed total"
+
+
+SMALL = [
+    ("bf16", 64, True), ("bf16", 64, False), ("bf16", 128, True), ("fp16", 128, False),
+    ("fp32", 64, True), ("fp32", 128, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_vs_oracle(gpu, case):
+    dt, d, causal = case
+    lens = [5, 1, 130, 257, 0, 64, 200]
+    announce(f"varlen small {case} lens={lens}")
+    inp = W.varlen_inputs(lens, lens, 3, d, dt, seed=300 + d)
+    o, lse = _run(inp, 3, d, 1 / np.sqrt(d), causal, gpu)
+    _check_all(inp, o, lse, 1 / np.sqrt(d), causal, dt)
+
+
+def test_unequal_q_kv_lengths_and_dead_rows(gpu):
+    """Query and key lengths differ per sequence; a sequence with no keys gives dead rows."""
+    lens_q = [40, 3, 129, 0, 70]
+    lens_kv = [90, 0, 64, 10, 300]
+    announce(f"varlen unequal q={lens_q} kv={lens_kv}")
+    inp = W.varlen_inputs(lens_q, lens_kv, 2, 64, "bf16", seed=401)
+    for causal in (False, True):
+        o, lse = _run(inp, 2, 64, 0.125, causal, gpu)
+        _check_all(inp, o, lse, 0.125, causal, "bf16")
+
+
+def test_loose_max_seqlen_bound(gpu):
+    """max_seqlen_q larger than the longest sequence only adds empty tiles."""
+    lens = [33, 250, 17]
+    announce("varlen loose bound")
+    inp = W.varlen_inputs(lens, lens, 2, 128, "bf16", seed=402)
+    o, lse = _run(inp, 2, 128, 0.1, True, gpu, max_q=inp.total_q, max_kv=4096)
+    _check_all(inp, o, lse, 0.1, True, "bf16")
+
+
+def test_workload_varlen_32seq_sampled(gpu):
+    """The packed workload at full size: 32 sequences, h16 d128, causal bf16."""
+    c = W.VARLEN_BF16_32SEQ_H16D128
+    inp = W.varlen_case_inputs(c)
+    announce(f"{c.name} T={inp.total_q}")
+    o, lse = _run(inp, c.h, c.d, c.scale, c.causal, gpu)
+    tq = inp.total_q
+    o64, l64 = f64(o[:tq]), f64(lse[:tq])
+    assert np.all(np.isfinite(o64)), "NaN from the poisoned capacity tail reached O"
+    assert torch.all(o[tq:] == 77.0) and torch.all(lse[tq:] == 55.0)
+    lens = inp.lens_q.numpy()
+    cu = inp.cu_q.numpy()
+    pick = sorted({0, len(lens) - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    rng = np.random.default_rng(9)
+    q64, k64, v64 = f64(inp.q[:tq]), f64(inp.k[:tq]), f64(inp.v[:tq])
+    for n in pick:
+        L = int(lens[n])
+        rows = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 24)]))
+        for hi in (0, 7, 15):
+            s0 = int(cu[n])
+            o_ref, l_ref = oracle.attn_rows(q64[s0 + rows, hi], rows, k64[s0:s0 + L, hi],
+                                            v64[s0:s0 + L, hi], c.scale, True)
+            check_o(o64[s0 + rows, hi], o_ref, "bf16", what=f"O[seq{n},h{hi}]")
+            check_lse(l64[s0 + rows, hi], l_ref, what=f"LSE[seq{n},h{hi}]")
