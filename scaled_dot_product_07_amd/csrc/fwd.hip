@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "sdpa_internal.h"
 
 namespace sdpa07 {
@@ -57,6 +59,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+// Buffer resource word 3 for raw (untyped) loads on gfx9-family parts, and an
+// offset past any num_records bound (such loads return zeros).
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kOutOfRange = (int)0x80000000u;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Mfma16;
@@ -85,6 +92,44 @@ __device__ __forceinline__ float other_half(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pins the computation of x to this point of the instruction stream (an empty
+// volatile asm that "modifies" x: its producers are emitted before it and its
+// users after it). Used to keep softmax work interleaved with MFMAs.
+template <typename X>
+__device__ __forceinline__ void pin(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Pack2;
+template <>
+struct Pack2<__bf16> {
+  using type = bf16x2;
+};
+template <>
+struct Pack2<_Float16> {
+  using type = f16x2;
+};
+
+// acc + h.x + h.y for a packed pair of 16-bit values (one v_dot2 with ones).
+template <typename T>
+__device__ __forceinline__ float dot2_ones(typename Pack2<T>::type h, float acc);
+template <>
+__device__ __forceinline__ float dot2_ones<__bf16>(bf16x2 h, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(h, one, acc, false);
+}
+template <>
+__device__ __forceinline__ float dot2_ones<_Float16>(f16x2 h, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(h, one, acc, false);
+}
 
 // Decoded work unit of one workgroup.
 struct Unit {
@@ -176,34 +221,92 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int
 
 // ---------------------------------------------------------------------------
 // fp16 / bf16 io.
+//
+// A workgroup of 8 waves owns a PAIR of 128-row query tiles of one head: tile
+// i (waves 0-3) and tile n-1-i (waves 4-7). Under the causal mask their key
+// counts sum to the same total for every pair, so every workgroup (and every
+// SIMD, which runs one wave of each tile) gets the same work; the key tiles
+// the short tile needs are a prefix of the long tile's and are loaded once.
+//
+// Per wave and key tile the work is software-pipelined: the QK^T products of
+// tile j+1 are issued in the same basic block as the softmax of tile j, so
+// the exp/convert/max VALU work fills the MFMA pipeline's issue gaps; the
+// P.V products of tile j then overlap the row sums. The running max used as
+// the exponent offset is only raised when a tile's max exceeds it by more
+// than kTau (log2 units), so P <= 2^kTau and the O accumulator is rescaled
+// only on those (rare) tiles; the result is exact either way because O and l
+// always share the same offset.
+constexpr float kTau = 8.f;
+
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kFwdThreads) fwd16_kernel(FwdParams p) {
+__global__ void __launch_bounds__(kFwdThreads16) fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
+  constexpr int NT = kFwdThreads16;
   constexpr int PITCH = D + 8;  // LDS row pitch (elements); +16 B breaks bank aliasing
   constexpr int CH_ROW = D / 8;  // 16-byte chunks per row
-  constexpr int CPT = BN * CH_ROW / kFwdThreads;  // chunks per thread per tensor
+  constexpr int CPT = BN * CH_ROW / NT;  // chunks per thread per tensor per tile
+  static_assert(CPT >= 1, "tile too small for the workgroup");
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  __shared__ __attribute__((aligned(16))) T lds[2][2][BN * PITCH];
+  __shared__ __attribute__((aligned(16))) T kl[2][BN * PITCH];
+  __shared__ __attribute__((aligned(16))) T vl[2][BN * PITCH];
 
-  const Unit w = decode_unit<VARLEN>(p);
-  if (w.qt * BM >= w.q_len) return;  // uniform over the workgroup, before any barrier
+  // ---- work unit: (pair of query tiles, b|sequence, h)
+  const int nbh = p.b * p.h;
+  const int pair = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int bi = bh / p.h, hi = bh % p.h;
+  int q_len, kv_len;
+  int64_t q_off, k_off, v_off, o_off, lse_off, lse_st;
+  if constexpr (VARLEN) {
+    const int q0 = min(max(p.cu_q[bi], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[bi + 1], 0), p.total_q);
+    const int k0 = min(max(p.cu_kv[bi], 0), p.total_kv);
+    const int k1 = min(max(p.cu_kv[bi + 1], 0), p.total_kv);
+    q_len = max(q1 - q0, 0);
+    kv_len = max(k1 - k0, 0);
+    q_off = (int64_t)q0 * p.q_ss + (int64_t)hi * p.q_sh;
+    o_off = (int64_t)q0 * p.o_ss + (int64_t)hi * p.o_sh;
+    k_off = (int64_t)k0 * p.k_ss + (int64_t)hi * p.k_sh;
+    v_off = (int64_t)k0 * p.v_ss + (int64_t)hi * p.v_sh;
+    lse_off = (int64_t)q0 * p.h + hi;
+    lse_st = p.h;
+  } else {
+    q_len = p.s_q;
+    kv_len = p.s_kv;
+    q_off = (int64_t)bi * p.q_sb + (int64_t)hi * p.q_sh;
+    o_off = (int64_t)bi * p.o_sb + (int64_t)hi * p.o_sh;
+    k_off = (int64_t)bi * p.k_sb + (int64_t)hi * p.k_sh;
+    v_off = (int64_t)bi * p.v_sb + (int64_t)hi * p.v_sh;
+    lse_off = ((int64_t)bi * p.h + hi) * p.s_q;
+    lse_st = 1;
+  }
+  const int n_qt = (q_len + BM - 1) / BM;
+  const int qa = pair, qb = n_qt - 1 - pair;
+  if (qa > qb) return;  // uniform over the workgroup, before any barrier
 
-  const T* __restrict__ Q = (const T*)p.q + w.q_off;
-  const T* __restrict__ K = (const T*)p.k + w.k_off;
-  const T* __restrict__ V = (const T*)p.v + w.v_off;
-  T* __restrict__ O = (T*)p.o + w.o_off;
+  const T* __restrict__ Q = (const T*)p.q + q_off;
+  const T* __restrict__ K = (const T*)p.k + k_off;
+  const T* __restrict__ V = (const T*)p.v + v_off;
+  T* __restrict__ O = (T*)p.o + o_off;
 
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  // wave-uniform values live in SGPRs so per-wave control flow stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hf = lane / 32, col = lane % 32;
-  const int row0 = w.qt * BM + wave * 32;  // first query row of this wave
-  const int qi = row0 + col;               // this lane's query row
-  const bool q_valid = qi < w.q_len;
-  const bool wave_active = row0 < w.q_len;
-  const int blk_last_q = min(w.q_len, (w.qt + 1) * BM) - 1;
-  const int kv_end = CAUSAL ? min(w.kv_len, blk_last_q + 1) : w.kv_len;
+  const int grp = wave / 4;
+  const bool grp_active = grp == 0 || qb != qa;  // a middle tile is owned by group 0
+  const int qt = grp == 0 ? qa : qb;
+  const int row0 = qt * BM + (wave % 4) * 32;
+  const int qi = row0 + col;
+  const bool wave_active = grp_active && row0 < q_len;
+  const bool q_valid = wave_active && qi < q_len;
+  const int last_q = min(q_len, (qb + 1) * BM) - 1;
+  const int kv_end = CAUSAL ? min(kv_len, last_q + 1) : kv_len;
   const int n_tiles = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = CAUSAL ? min(w.kv_len, min(w.q_len, row0 + 32)) : w.kv_len;
+  const int wave_kv_end =
+      !wave_active ? 0 : (CAUSAL ? min(kv_len, min(q_len, row0 + 32)) : kv_len);
+  const int wave_tiles = (wave_kv_end + BN - 1) / BN;
 
   // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7].
   v8 qf[D / 16];
@@ -218,91 +321,252 @@ __global__ void __launch_bounds__(kFwdThreads) fwd16_kernel(FwdParams p) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float l_run = 0.f;
   const float c = p.scale_log2;
 
+  // K/V tile loads through a buffer resource rebased per tile: rows at or
+  // past the sequence's key count get an out-of-range offset and read as
+  // zeros, without a branch (and without touching memory past the keys).
+  int kroff[CPT], vroff[CPT], lrow[CPT];
+#pragma unroll
+  for (int x = 0; x < CPT; ++x) {
+    const int ch = tid + NT * x;
+    lrow[x] = ch / CH_ROW;
+    const int cc = ch % CH_ROW;
+    kroff[x] = lrow[x] * (int)p.k_ss * (int)sizeof(T) + cc * 16;
+    vroff[x] = lrow[x] * (int)p.v_ss * (int)sizeof(T) + cc * 16;
+  }
   i16x8 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
+  auto gload = [&](i16x8(&reg)[CPT], const T* __restrict__ base, int64_t stride,
+                   const int(&roff)[CPT], int j) {
+    const T* tb = base + (int64_t)j * BN * stride;
+    const int rows = kv_len - j * BN;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, 0x7fffffff, kBufferFlags);
 #pragma unroll
     for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + kFwdThreads * x;
-      const int r = ch / CH_ROW, cc = ch % CH_ROW;
-      const int key = j * BN + r;
-      if (key < w.kv_len) {
-        kreg[x] = *(const i16x8*)(K + (int64_t)key * p.k_ss + cc * 8);
-        vreg[x] = *(const i16x8*)(V + (int64_t)key * p.v_ss + cc * 8);
-      } else {
-        kreg[x] = i16x8{};
-        vreg[x] = i16x8{};
-      }
+      const int off = lrow[x] < rows ? roff[x] : kOutOfRange;
+      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
   };
-  auto store_tile = [&](int buf) {
+  auto lstore = [&](T* buf, const i16x8(&reg)[CPT]) {
 #pragma unroll
     for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + kFwdThreads * x;
+      const int ch = tid + NT * x;
       const int r = ch / CH_ROW, cc = ch % CH_ROW;
-      *(i16x8*)&lds[buf][0][r * PITCH + cc * 8] = kreg[x];
-      *(i16x8*)&lds[buf][1][r * PITCH + cc * 8] = vreg[x];
+      *(i16x8*)&buf[r * PITCH + cc * 8] = reg[x];
+    }
+  };
+  // Softmax state (per lane = per query row, both halves agree):
+  //   m_cur  offset of P_j (log2 units) for the tile the next block exponentiates
+  //   a_cur  2^(m_prev - m_cur): factor for l (in that block) and for O (after it)
+  //   m_prev offset of the previous tile (kept to redo the update after a mask)
+  //   m_l    offset of l (and of O once the pending P.V is added): the LSE base
+  float m_prev = -INFINITY, m_cur = -INFINITY, a_cur = 0.f, m_l = -INFINITY;
+  // lazy offset update from a tile max (raw score units): raise the offset
+  // only when the tile's max exceeds it by more than kTau
+  auto offset_update = [&](float mx, float m_from, float& m_to, float& a) {
+    const float mt = mx * c;
+    const float m_new = mt > m_from + kTau ? mt : m_from;
+    a = fast_exp2(m_from - (m_new == -INFINITY ? 0.f : m_new));
+    m_to = m_new;
+  };
+  auto row_max = [&](const f32x16(&sv)[2]) -> float {
+    float a = fmaxf(sv[0][0], sv[0][1]), b = fmaxf(sv[1][0], sv[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      a = fmaxf(a, fmaxf(sv[0][r], sv[0][r + 1]));
+      b = fmaxf(b, fmaxf(sv[1][r], sv[1][r + 1]));
+    }
+    const float mx = fmaxf(a, b);
+    return fmaxf(mx, other_half(mx));
+  };
+
+  // One pipeline block for key tile j of this wave, straight-line code:
+  //   QK  : S_{j+1} = K_{j+1} Q^T                (MFMAs 0 .. NQK-1)
+  //   PV  : O^T += V_{j-1}^T P_{j-1}^T             (MFMAs NQK .. NM-1)
+  //   SM  : P_j = 2^(c S_j - m_cur), row sum into l (VALU, early chunks)
+  //   MX  : row max of S_{j+1} and the next offset (VALU, last chunks, once
+  //         the QK results are complete)
+  // It is emitted as NM chunks, each = the LDS read for the MFMA PF chunks
+  // ahead, one MFMA, and a slice of the VALU work; the slices are pinned to
+  // their chunk so the VALU work issues while the MFMA pipe is busy.
+  constexpr int NQK = 2 * (D / 16);
+  constexpr int NPV = 4 * (D / 32);
+  constexpr int NM = NQK + NPV;
+  constexpr int PF = 3;                                   // LDS read-ahead (chunks)
+  constexpr int NPAIR = 16;                               // 32 scores per lane, in pairs
+  constexpr int EXP_CHUNKS = NM - 6 < 16 ? NM - 6 : 16;   // chunks holding the exps
+  constexpr int MX0 = NM - 4;                             // chunks MX0 .. MX0+2: max of S_{j+1}
+  const int vrow = 4 * hf + (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+  auto block = [&](const T* kb, const T* vb, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+                   const v8(&p_prev)[4], v8(&p_cur)[4]) {
+    auto read_op = [&](int i) -> v8 {
+      if (i < NQK) {
+        const int ks = i / 2, mb = i % 2;
+        return *(const v8*)&kb[(32 * mb + col) * PITCH + 16 * ks + 8 * hf];
+      }
+      const int t = (i - NQK) / (D / 32), db = (i - NQK) % (D / 32);
+      const T* a0 = vb + (16 * t + vrow) * PITCH + 32 * db + vcol;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(a0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(a0 + 8 * PITCH));
+      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
+    m_l = m_cur;
+    float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
+    i32x4 pk[4];
+    auto slice = [&](int i) {
+      if (i < EXP_CHUNKS) {
+        const int p0 = i * NPAIR / EXP_CHUNKS, p1 = (i + 1) * NPAIR / EXP_CHUNKS;
+#pragma unroll
+        for (int pp = p0; pp < p1; ++pp) {
+          const int t = pp / 4, e2 = pp % 4;
+          const f32x2 x = {fast_exp2(fmaf(s_cur[t / 2][8 * (t % 2) + 2 * e2], c, -m_off)),
+                           fast_exp2(fmaf(s_cur[t / 2][8 * (t % 2) + 2 * e2 + 1], c, -m_off))};
+          const auto h = __builtin_convertvector(x, typename Pack2<T>::type);
+          int hb = __builtin_bit_cast(int, h);
+          pin(hb);
+          pk[t][e2] = hb;
+          if (e2 & 1) r1 = dot2_ones<T>(h, r1);
+          else r0 = dot2_ones<T>(h, r0);
+        }
+      }
+      if (i == EXP_CHUNKS) {
+        l_run = l_run * a_cur + (r0 + r1);
+        pin(l_run);
+      }
+      if (i == MX0) {
+        mxa = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), fmaxf(s_nxt[0][2], s_nxt[0][3]));
+        mxb = fmaxf(fmaxf(s_nxt[0][4], s_nxt[0][5]), fmaxf(s_nxt[0][6], s_nxt[0][7]));
+#pragma unroll
+        for (int r = 8; r < 16; r += 2) {
+          mxa = fmaxf(mxa, s_nxt[0][r]);
+          mxb = fmaxf(mxb, s_nxt[0][r + 1]);
+        }
+        pin(mxa);
+        pin(mxb);
+      }
+      if (i == MX0 + 1) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          mxa = fmaxf(mxa, s_nxt[1][r]);
+          mxb = fmaxf(mxb, s_nxt[1][r + 1]);
+        }
+        pin(mxa);
+        pin(mxb);
+      }
+      if (i == MX0 + 2) {
+        float mx = fmaxf(mxa, mxb);
+        mx = fmaxf(mx, other_half(mx));
+        m_prev = m_cur;
+        offset_update(mx, m_cur, m_cur, a_cur);
+        pin(m_cur);
+        pin(a_cur);
+      }
+    };
+    v8 op[NM];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) op[i] = read_op(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + PF < NM) op[i + PF] = read_op(i + PF);
+      if (i < NQK) {
+        const int ks = i / 2, mb = i % 2;
+        s_nxt[mb] = M::mma(op[i], qf[ks], ks == 0 ? f32x16{} : s_nxt[mb]);
+      } else {
+        const int t = (i - NQK) / (D / 32), db = (i - NQK) % (D / 32);
+        acc[db] = M::mma(op[i], p_prev[t], acc[db]);
+      }
+      slice(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p_cur[t] = __builtin_bit_cast(v8, pk[t]);
+  };
+
+  // The per-tile step. Every pipeline block runs the same fused code; the
+  // edges are neutralised by data instead of separate code paths: a zero
+  // P_{j-1} (and a zeroed V buffer) makes PV a no-op, a fully masked S_j
+  // makes the softmax a no-op (P = 0), and an unneeded QK only computes a
+  // value that is never used. A wave skips the tiles past its causal range
+  // (j > wave_tiles) except for the memory work the whole workgroup shares.
+  auto step = [&](int j, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
+                  v8(&p_cur)[4]) {
+    // K_{j+1} into LDS (its global load was issued one block ago); the
+    // loads and stores run unconditionally so that wait counts stay exact (a
+    // load past the keys reads zeros through the buffer bound)
+    lstore(kl[(j + 1) & 1], kreg);
+    __syncthreads();
+    lstore(vl[j & 1], vreg);
+    gload(vreg, V, p.v_ss, vroff, j + 1);
+    gload(kreg, K, p.k_ss, kroff, j + 2);
+    if (j <= wave_tiles) {
+      const int kbase = j * BN;
+      // keys at or past kv_lim are masked: all of them once the wave is past its range
+      const int kv_lim = j < wave_tiles ? kv_len : 0;
+      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_lim) {
+        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_lim, hf);
+        offset_update(row_max(s_cur), m_prev, m_cur, a_cur);  // redo with the mask
+      }
+      const bool rescale = __any(a_cur != 1.f);
+      const float a_blk = a_cur;
+      block(kl[(j + 1) & 1], vl[(j - 1) & 1], s_cur, s_nxt, p_prev, p_cur);
+      if (rescale) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
+      }
     }
   };
 
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-    const int kbase = j * BN;
-    if (wave_active && kbase < wave_kv_end) {
-      // S^T (64 keys x 32 queries) = K_tile Q^T.
-      f32x16 s[2];
+    f32x16 sa[2], sb[2];
+    v8 pa[4], pb[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const v8 a = *(const v8*)&lds[buf][0][(32 * mb + col) * PITCH + 16 * ks + 8 * hf];
-          s[mb] = M::mma(a, qf[ks], s[mb]);
-        }
-      }
-      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > w.kv_len)
-        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf);
-      const float alpha = softmax_tile(s, c, m_run, l_run);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-
-      // P^T as B operands: MFMA t covers keys 16t + 8(e/4) + 4hf + e%4.
-      v8 pf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[t][e] = (T)s[t / 2][8 * (t % 2) + e];
-
-      // O^T += V^T P^T. The transposing LDS read gives lane (16-group g,
-      // index i) V[kb + 0..3][dcol + i] with kb = 16t + 4hf, which is the
-      // A operand for the same key relabelling.
-      const T* vb = &lds[buf][1][0];
-      const int vrow = 4 * hf + (lane % 16) / 4;
-      const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const T* a0 = vb + (16 * t + vrow) * PITCH + 32 * db + vcol;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0 + 8 * PITCH));
-          const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[db] = M::mma(__builtin_bit_cast(v8, a), pf[t], acc[db]);
-        }
+    for (int t = 0; t < 4; ++t) {
+      pa[t] = v8{};
+      pb[t] = v8{};
     }
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    gload(kreg, K, p.k_ss, kroff, 0);
+    gload(vreg, V, p.v_ss, vroff, 0);
+    lstore(kl[0], kreg);
+    {
+      const i16x8 zero[CPT] = {};
+      lstore(vl[1], zero);  // read by the no-op P.V of the first block
+    }
+    gload(kreg, K, p.k_ss, kroff, 1);
     __syncthreads();
+    // S_0 = QK(K_0) and its offset; the P.V and softmax parts are neutralised
+    // (sb fully masked, P_{-1} = 0, V buffer 1 zero)
+    mask_tile<CAUSAL>(sb, 0, qi, 0, hf);
+    block(kl[0], vl[1], sb, sa, pb, pa);
+    int j = 0;
+    for (; j + 1 < n_tiles; j += 2) {
+      step(j, sa, sb, pb, pa);
+      step(j + 1, sb, sa, pa, pb);
+    }
+    if (j < n_tiles) {
+      step(j, sa, sb, pb, pa);
+      ++j;
+    }
+    // drain: P.V of the last tile, whose V was stored in the last block; the
+    // block's softmax is neutralised (masked scores, factor 1 at the offset
+    // of l), and its new offset comes from unused scores and is discarded
+    __syncthreads();
+    if (j - 1 < wave_tiles) {
+      m_cur = m_l;
+      a_cur = 1.f;
+      if ((j - 1) & 1) {
+        mask_tile<CAUSAL>(sa, 0, qi, 0, hf);
+        block(kl[0], vl[1], sa, sb, pb, pa);
+      } else {
+        mask_tile<CAUSAL>(sb, 0, qi, 0, hf);
+        block(kl[0], vl[0], sb, sa, pa, pb);
+      }
+    }
   }
 
   // Epilogue: combine the two halves' partial sums, normalise, store.
@@ -321,8 +585,8 @@ __global__ void __launch_bounds__(kFwdThreads) fwd16_kernel(FwdParams p) {
         *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
       }
     if (hf == 0 && p.lse)
-      p.lse[w.lse_off + (int64_t)qi * w.lse_st] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[lse_off + (int64_t)qi * lse_st] =
+          l_tot > 0.f ? (m_l + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -458,6 +722,8 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 const void* pick_kernel(Dt dt) {
+  // fp16/bf16 kernels run 8-wave workgroups over pairs of query tiles;
+  // the fp32 kernel runs 4-wave workgroups over single query tiles.
   switch (dt) {
     case Dt::BF16: return (const void*)&fwd16_kernel<__bf16, D, CAUSAL, VARLEN>;
     case Dt::F16: return (const void*)&fwd16_kernel<_Float16, D, CAUSAL, VARLEN>;
@@ -479,11 +745,14 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   const void* fn = d == 64 ? pick_kernel<64>(dt, causal, varlen)
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
-  const long long grid = (long long)p.n_qtiles * p.b * p.h;
+  const bool paired = dt != Dt::F32;
+  const long long units = paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  const long long grid = units * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kFwdThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(paired ? kFwdThreads16 : kFwdThreads),
+                         args, 0, stream);
 }
 
 }  // namespace sdpa07
