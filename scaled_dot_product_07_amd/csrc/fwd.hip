@@ -239,7 +239,8 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kFwdThreads16) fwd16_kernel(FwdParams p) {
+__global__ void __launch_bounds__(kFwdThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int NT = kFwdThreads16;
   constexpr int PITCH = D + 8;  // LDS row pitch (elements); +16 B breaks bank aliasing
@@ -251,10 +252,15 @@ __global__ void __launch_bounds__(kFwdThreads16) fwd16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) T kl[2][BN * PITCH];
   __shared__ __attribute__((aligned(16))) T vl[2][BN * PITCH];
 
-  // ---- work unit: (pair of query tiles, b|sequence, h)
+  // ---- work unit: (query tile, b|sequence, h). Query tiles are ordered as a
+  // snake, heaviest causal tile first: n-1, n-2, .., n/2, then 0, 1, .., so the
+  // two workgroups resident on a CU (dispatched nbh*ceil(n/2) apart) pair a
+  // heavy tile with a light one.
   const int nbh = p.b * p.h;
-  const int pair = blockIdx.x / nbh;
+  const int urow = blockIdx.x / nbh;
   const int bh = blockIdx.x % nbh;
+  const int half = (p.n_qtiles + 1) / 2;
+  const int qt_sched = urow < half ? p.n_qtiles - 1 - urow : urow - half;
   const int bi = bh / p.h, hi = bh % p.h;
   int q_len, kv_len;
   int64_t q_off, k_off, v_off, o_off, lse_off, lse_st;
@@ -281,9 +287,7 @@ __global__ void __launch_bounds__(kFwdThreads16) fwd16_kernel(FwdParams p) {
     lse_off = ((int64_t)bi * p.h + hi) * p.s_q;
     lse_st = 1;
   }
-  const int n_qt = (q_len + BM - 1) / BM;
-  const int qa = pair, qb = n_qt - 1 - pair;
-  if (qa > qb) return;  // uniform over the workgroup, before any barrier
+  if (qt_sched * BM >= q_len) return;  // uniform over the workgroup, before any barrier
 
   const T* __restrict__ Q = (const T*)p.q + q_off;
   const T* __restrict__ K = (const T*)p.k + k_off;
@@ -294,14 +298,12 @@ __global__ void __launch_bounds__(kFwdThreads16) fwd16_kernel(FwdParams p) {
   // wave-uniform values live in SGPRs so per-wave control flow stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hf = lane / 32, col = lane % 32;
-  const int grp = wave / 4;
-  const bool grp_active = grp == 0 || qb != qa;  // a middle tile is owned by group 0
-  const int qt = grp == 0 ? qa : qb;
-  const int row0 = qt * BM + (wave % 4) * 32;
+  const int qt = qt_sched;
+  const int row0 = qt * BM + wave * 32;
   const int qi = row0 + col;
-  const bool wave_active = grp_active && row0 < q_len;
+  const bool wave_active = row0 < q_len;
   const bool q_valid = wave_active && qi < q_len;
-  const int last_q = min(q_len, (qb + 1) * BM) - 1;
+  const int last_q = min(q_len, (qt + 1) * BM) - 1;
   const int kv_end = CAUSAL ? min(kv_len, last_q + 1) : kv_len;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int wave_kv_end =
@@ -746,8 +748,7 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
   const bool paired = dt != Dt::F32;
-  const long long units = paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
-  const long long grid = units * p.b * p.h;
+  const long long grid = (long long)p.n_qtiles * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};
