@@ -103,8 +103,9 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int causal, void* stream);
 
 /*
- * Bytes of device workspace sdpa_bwd needs for these sizes (fp32 row
- * statistics, 256-byte aligned). The caller allocates it.
+ * Bytes of device workspace sdpa_bwd needs for these sizes: two fp32 values
+ * per query row (rowsum(dO * O) and the statistic in base 2), rounded up to
+ * 256 bytes. The caller allocates it (256-byte aligned).
  */
 size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype);
 

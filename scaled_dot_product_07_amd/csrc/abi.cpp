@@ -209,8 +209,7 @@ size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype) {
   (void)d;
   (void)dtype;
   if (b <= 0 || h <= 0 || s_q <= 0) return 256;
-  const size_t bytes = (size_t)b * h * s_q * sizeof(float);
-  return (bytes + 255) / 256 * 256;
+  return sdpa07::bwd_workspace_bytes((long long)b * h * s_q);
 }
 
 sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -1,6 +1,524 @@
-// Backward kernels (placeholder until the dK/dV and dQ passes land).
+// Scaled-dot-product attention backward for gfx950 (MI355X).
+//
+// Given Q, K, V, O, dO and the forward's row statistic LSE, computes
+//   P = exp(scale * Q K^T - LSE)  (the forward's softmax, recomputed),
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q
+// (cudnn-frontend PR #554: the dense backward returns dQ, dK, dV from Q, K, V,
+// O, dO and the statistic; its merge log, the SM80 backward TemplateParams
+// entry: the chain starts with the dO.O row dot product, then the main pass
+// and the dQ pass).
+//
+// Three kernels, in order on one stream, no atomics (bit-identical results
+// run to run):
+//   bwd_pre   D = rowsum(dO * O) and LSE in base 2 (LSE * log2 e; +inf for a
+//             row without visible keys so that its P is 0), one pass over
+//             dO and O;
+//   bwd_dkdv  one wave per 32 keys: its K and V rows stay in VGPRs as MFMA B
+//             operands, and 64-query tiles of Q, dO (with their LSE and D)
+//             stream through double-buffered LDS. Per tile: S = Q K^T and
+//             dP = dO V^T (the lane owns one key column), P and dS in VGPRs,
+//             then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//             through the transposing LDS read ds_read_b64_tr_b16;
+//   bwd_dq    one wave per 32 queries: its Q and dO rows stay in VGPRs, and
+//             64-key tiles of K, V stream through LDS. Per tile: S^T = K Q^T
+//             and dP^T = V dO^T (the lane owns one query), dS^T in VGPRs, then
+//             dQ^T += K^T dS^T.
+// The contraction index of the second products is relabelled exactly as in
+// the forward (P, dS go from the MFMA C layout to B operands in registers).
+// Causal (top-left) masking skips fully hidden tiles and masks the diagonal
+// ones; rows past the sequence read as zeros through buffer bounds.
+
+#include "kernel_common.h"
 #include "sdpa_internal.h"
 
 namespace sdpa07 {
-hipError_t launch_bwd(const BwdParams&, Dt, int, bool, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPreThreads = 256;
+constexpr int kBwdThreads = 256;
+constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave)
+constexpr int kDkdvQ = 64;      // queries per streamed tile
+constexpr int kDqRows = 128;    // queries per dQ workgroup (32 per wave)
+constexpr int kDqK = 64;        // keys per streamed tile
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x) {
+  return (float)x;
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O) in fp32 and LSE in base 2. D/8 lanes per row.
+template <typename T, int D>
+__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2) {
+  constexpr int LPR = D / 8;  // lanes per row
+  constexpr int RPB = kPreThreads / LPR;
+  const int tid = threadIdx.x;
+  const long long r = (long long)blockIdx.x * RPB + tid / LPR;
+  const long long n = (long long)p.b * p.h * p.s_q;
+  const int sub = tid % LPR;
+  float acc = 0.f;
+  if (r < n) {
+    const int si = (int)(r % p.s_q);
+    const long long bh = r / p.s_q;
+    const int hi = (int)(bh % p.h), bi = (int)(bh / p.h);
+    const T* o = (const T*)p.o + bi * p.o_sb + hi * p.o_sh + (long long)si * p.o_ss + sub * 8;
+    const T* g =
+        (const T*)p.dout + bi * p.do_sb + hi * p.do_sh + (long long)si * p.do_ss + sub * 8;
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    const t8 ov = *(const t8*)o, gv = *(const t8*)g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(to_f(ov[e]), to_f(gv[e]), acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPR);
+  if (r < n && sub == 0) {
+    p.delta[r] = acc;
+    const float l = p.lse[r];
+    lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// Transposing LDS read of an A operand: lane (16-group g, index i) receives
+// rows rbase + 4hf + 0..3 and + 8 .. 11 of column cbase + 16(g%2) + i.
+template <typename T, int PITCH>
+__device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row, int colv) {
+  const T* a0 = base + row * PITCH + colv;
+  const i16x4 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(a0 + 8 * PITCH));
+  return __builtin_bit_cast(typename Mfma16<T>::v8,
+                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Packs 32 fp32 values held in a [2] x 16 MFMA C layout into 4 B operands
+// for a 64-deep contraction (element e of MFMA t: register 8(t%2)+e of block t/2).
+template <typename T>
+__device__ __forceinline__ void pack_b(const f32x16 (&x)[2], typename Mfma16<T>::v8 (&out)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    i32x4 pk;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const f32x2 v = {x[t / 2][8 * (t % 2) + 2 * e2], x[t / 2][8 * (t % 2) + 2 * e2 + 1]};
+      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
+    }
+    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
+  }
+}
+
+// Loads one tile of `ROWS` rows x D of a (rows, d) tensor whose row r is at
+// base + r * stride, rows at or past `rows` reading as zeros.
+template <typename T, int D, int ROWS, int NT>
+struct TileLoader {
+  static constexpr int CH = D / 8;
+  static constexpr int CPT = ROWS * CH / NT;
+  int roff[CPT], lrow[CPT], lofs[CPT];
+  __device__ void init(int tid, int64_t stride, int pitch) {
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) {
+      const int ch = tid + NT * x;
+      lrow[x] = ch / CH;
+      roff[x] = lrow[x] * (int)stride * (int)sizeof(T) + (ch % CH) * 16;
+      lofs[x] = lrow[x] * pitch + (ch % CH) * 8;
+    }
+  }
+  __device__ void load(i16x8 (&reg)[CPT], const T* tile_base, int rows) const {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile_base, (short)0, 0x7fffffff, kBufferFlags);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) {
+      const int off = lrow[x] < rows ? roff[x] : kOutOfRange;
+      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  }
+  __device__ void store(T* lds, const i16x8 (&reg)[CPT]) const {
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) *(i16x8*)&lds[lofs[x]] = reg[x];
+  }
+};
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, const float* lse2) {
+  constexpr int BQ = kDkdvQ, PITCH = D + 8;
+  using M = Mfma16<T>;
+  using v8 = typename M::v8;
+  using LQ = TileLoader<T, D, BQ, kBwdThreads>;
+  __shared__ __attribute__((aligned(16))) T ql[2][BQ * PITCH];
+  __shared__ __attribute__((aligned(16))) T gl[2][BQ * PITCH];
+  __shared__ __attribute__((aligned(16))) float l2l[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dll[2][BQ];
+
+  const int nbh = p.b * p.h;
+  const int kt = blockIdx.x / nbh;  // key tile; the first ones see the most queries
+  const int bh = blockIdx.x % nbh;
+  const int bi = bh / p.h, hi = bh % p.h;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int hf = lane / 32, col = lane % 32;
+  const int key0 = kt * kDkdvKeys + wave * 32;  // first key of this wave
+  const int kj = key0 + col;                     // this lane's key
+  if (kt * kDkdvKeys >= p.s_kv) return;
+
+  const T* Q = (const T*)p.q + bi * p.q_sb + hi * p.q_sh;
+  const T* G = (const T*)p.dout + bi * p.do_sb + hi * p.do_sh;
+  const T* K = (const T*)p.k + bi * p.k_sb + hi * p.k_sh;
+  const T* V = (const T*)p.v + bi * p.v_sb + hi * p.v_sh;
+  const float* L2 = lse2 + (int64_t)bh * p.s_q;
+  const float* DL = p.delta + (int64_t)bh * p.s_q;
+  const float c = p.scale_log2;
+
+  // this lane's K and V rows as B operands (B[k = d][n = key])
+  v8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    i16x8 a = {}, b = {};
+    if (kj < p.s_kv) {
+      a = *(const i16x8*)(K + (int64_t)kj * p.k_ss + 16 * ks + 8 * hf);
+      b = *(const i16x8*)(V + (int64_t)kj * p.v_ss + 16 * ks + 8 * hf);
+    }
+    kf[ks] = __builtin_bit_cast(v8, a);
+    vf[ks] = __builtin_bit_cast(v8, b);
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int n_qt = (p.s_q + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? min(kt * kDkdvKeys / BQ, n_qt) : 0;  // first tile with a visible query
+  const int wave_t0 = CAUSAL ? key0 / BQ : 0;
+  LQ lq, lg;
+  lq.init(tid, p.q_ss, PITCH);
+  lg.init(tid, p.do_ss, PITCH);
+  i16x8 qr[LQ::CPT], gr[LQ::CPT];
+  float l2r = 0.f, dlr = 0.f;
+  auto gload = [&](int t) {
+    const int rows = p.s_q - t * BQ;
+    lq.load(qr, Q + (int64_t)t * BQ * p.q_ss, rows);
+    lg.load(gr, G + (int64_t)t * BQ * p.do_ss, rows);
+    if (tid < BQ) {
+      const int qrow = t * BQ + tid;
+      l2r = qrow < p.s_q ? L2[qrow] : INFINITY;
+      dlr = qrow < p.s_q ? DL[qrow] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+    lq.store(ql[buf], qr);
+    lg.store(gl[buf], gr);
+    if (tid < BQ) {
+      l2l[buf][tid] = l2r;
+      dll[buf][tid] = dlr;
+    }
+  };
+  const int vrow = 4 * hf + (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  if (t0 < n_qt) {
+    gload(t0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int t = t0; t < n_qt; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < n_qt) gload(t + 1);
+    if (t >= wave_t0) {
+      const T* qb_ = ql[buf];
+      const T* gb_ = gl[buf];
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const v8 aq = *(const v8*)&qb_[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
+          const v8 ag = *(const v8*)&gb_[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
+          s[qb] = M::mma(aq, kf[ks], s[qb]);
+          dp[qb] = M::mma(ag, vf[ks], dp[qb]);
+        }
+      }
+      // P and dS in the C layout: lane = key kj, register r of block qb =
+      // query t*BQ + 32qb + 8(r/4) + 4hf + r%4
+      const bool mask = CAUSAL && t * BQ < key0 + 31;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 l4 = *(const float4*)&l2l[buf][32 * qb + 8 * rq + 4 * hf];
+          const float4 d4 = *(const float4*)&dll[buf][32 * qb + 8 * rq + 4 * hf];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            float pv = fast_exp2(fmaf(s[qb][r], c, -lv[e]));
+            if (mask && t * BQ + 32 * qb + 8 * rq + 4 * hf + e < kj) pv = 0.f;
+            s[qb][r] = pv;
+            dp[qb][r] = pv * (dp[qb][r] - dd[e]);
+          }
+        }
+      v8 pb[4], sb[4];
+      pack_b<T>(s, pb);
+      pack_b<T>(dp, sb);
+      // dV^T += dO^T P, dK^T += Q^T dS (contraction over the 64 queries)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const v8 ag = read_tr<T, PITCH>(gb_, 16 * t4 + vrow, 32 * db + vcol);
+          const v8 aq = read_tr<T, PITCH>(qb_, 16 * t4 + vrow, 32 * db + vcol);
+          dv[db] = M::mma(ag, pb[t4], dv[db]);
+          dk[db] = M::mma(aq, sb[t4], dk[db]);
+        }
+    }
+    if (t + 1 < n_qt) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // store: lane owns key kj, d rows 32db + 8rq + 4hf + 0..3
+  if (kj < p.s_kv) {
+    T* dkp = (T*)p.dk + bi * p.dk_sb + hi * p.dk_sh + (int64_t)kj * p.dk_ss;
+    T* dvp = (T*)p.dv + bi * p.dv_sb + hi * p.dv_sh + (int64_t)kj * p.dv_ss;
+    typedef T t4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        t4v a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (T)(dk[db][4 * rq + e] * p.scale);
+          b[e] = (T)dv[db][4 * rq + e];
+        }
+        *(t4v*)(dkp + 32 * db + 8 * rq + 4 * hf) = a;
+        *(t4v*)(dvp + 32 * db + 8 * rq + 4 * hf) = b;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const float* lse2) {
+  constexpr int BK = kDqK, PITCH = D + 8;
+  using M = Mfma16<T>;
+  using v8 = typename M::v8;
+  using LK = TileLoader<T, D, BK, kBwdThreads>;
+  __shared__ __attribute__((aligned(16))) T kl[2][BK * PITCH];
+  __shared__ __attribute__((aligned(16))) T vl[2][BK * PITCH];
+
+  const int nbh = p.b * p.h;
+  const int n_qtiles = (p.s_q + kDqRows - 1) / kDqRows;
+  const int qt = n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest causal tiles first
+  const int bh = blockIdx.x % nbh;
+  const int bi = bh / p.h, hi = bh % p.h;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int hf = lane / 32, col = lane % 32;
+  const int row0 = qt * kDqRows + wave * 32;
+  const int qi = row0 + col;
+  const bool q_valid = qi < p.s_q;
+
+  const T* Q = (const T*)p.q + bi * p.q_sb + hi * p.q_sh;
+  const T* G = (const T*)p.dout + bi * p.do_sb + hi * p.do_sh;
+  const T* K = (const T*)p.k + bi * p.k_sb + hi * p.k_sh;
+  const T* V = (const T*)p.v + bi * p.v_sb + hi * p.v_sh;
+  const float c = p.scale_log2;
+  const float l2 = q_valid ? lse2[(int64_t)bh * p.s_q + qi] : INFINITY;
+  const float dl = q_valid ? p.delta[(int64_t)bh * p.s_q + qi] : 0.f;
+
+  v8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    i16x8 a = {}, b = {};
+    if (q_valid) {
+      a = *(const i16x8*)(Q + (int64_t)qi * p.q_ss + 16 * ks + 8 * hf);
+      b = *(const i16x8*)(G + (int64_t)qi * p.do_ss + 16 * ks + 8 * hf);
+    }
+    qf[ks] = __builtin_bit_cast(v8, a);
+    gf[ks] = __builtin_bit_cast(v8, b);
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  const int last_q = min(p.s_q, (qt + 1) * kDqRows) - 1;
+  const int kv_end = CAUSAL ? min(p.s_kv, last_q + 1) : p.s_kv;
+  const int n_tiles = (kv_end + BK - 1) / BK;
+  const int wave_kv_end = row0 >= p.s_q ? 0 : (CAUSAL ? min(p.s_kv, min(p.s_q, row0 + 32)) : p.s_kv);
+  LK lk, lv;
+  lk.init(tid, p.k_ss, PITCH);
+  lv.init(tid, p.v_ss, PITCH);
+  i16x8 kr[LK::CPT], vr[LK::CPT];
+  auto gload = [&](int j) {
+    lk.load(kr, K + (int64_t)j * BK * p.k_ss, p.s_kv - j * BK);
+    lv.load(vr, V + (int64_t)j * BK * p.v_ss, p.s_kv - j * BK);
+  };
+  const int vrow = 4 * hf + (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  if (n_tiles > 0) {
+    gload(0);
+    lk.store(kl[0], kr);
+    lv.store(vl[0], vr);
+  }
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) gload(j + 1);
+    const int kbase = j * BK;
+    if (kbase < wave_kv_end) {
+      const T* kb_ = kl[buf];
+      const T* vb_ = vl[buf];
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const v8 ak = *(const v8*)&kb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
+          const v8 av = *(const v8*)&vb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
+          s[kb] = M::mma(ak, qf[ks], s[kb]);
+          dp[kb] = M::mma(av, gf[ks], dp[kb]);
+        }
+      }
+      // lane = query qi; register r of block kb = key kbase + 32kb + 8(r/4) + 4hf + r%4
+      const bool mask = (CAUSAL && kbase + BK - 1 > row0) || kbase + BK > p.s_kv;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(fmaf(s[kb][r], c, -l2));
+          if (mask) {
+            const int key = kbase + 32 * kb + 8 * (r / 4) + 4 * hf + (r % 4);
+            if ((CAUSAL && key > qi) || key >= p.s_kv) pv = 0.f;
+          }
+          dp[kb][r] = pv * (dp[kb][r] - dl);
+        }
+      v8 sb[4];
+      pack_b<T>(dp, sb);
+      // dQ^T += K^T dS^T (contraction over the 64 keys)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const v8 ak = read_tr<T, PITCH>(kb_, 16 * t4 + vrow, 32 * db + vcol);
+          dq[db] = M::mma(ak, sb[t4], dq[db]);
+        }
+    }
+    if (j + 1 < n_tiles) {
+      lk.store(kl[buf ^ 1], kr);
+      lv.store(vl[buf ^ 1], vr);
+    }
+    __syncthreads();
+  }
+
+  if (q_valid) {
+    T* dqp = (T*)p.dq + bi * p.dq_sb + hi * p.dq_sh + (int64_t)qi * p.dq_ss;
+    typedef T t4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        t4v a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (T)(dq[db][4 * rq + e] * p.scale);
+        *(t4v*)(dqp + 32 * db + 8 * rq + 4 * hf) = a;
+      }
+  }
+}
+
+// Fills a (b, h, s, d) tensor with zeros (dK, dV when there are no queries,
+// dQ when there are no keys is covered by the dQ kernel itself).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) zero_rows_kernel(void* x, int64_t sb, int64_t sh,
+                                                        int64_t ss, int b, int h, int s) {
+  const long long r = (long long)blockIdx.x * (256 / (D / 8)) + threadIdx.x / (D / 8);
+  const int sub = threadIdx.x % (D / 8);
+  if (r >= (long long)b * h * s) return;
+  const int si = (int)(r % s);
+  const long long bh = r / s;
+  T* ptr = (T*)x + (bh / h) * sb + (bh % h) * sh + (int64_t)si * ss + sub * 8;
+  *(i16x8*)ptr = i16x8{};
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
+  BwdParams arg = p;
+  const long long n = (long long)p.b * p.h * p.s_q;
+  float* lse2 = p.delta + (n + 63) / 64 * 64;
+  const int nbh = p.b * p.h;
+  hipError_t e;
+  if (p.s_q == 0 || p.s_kv == 0) {
+    // nothing to recompute: every gradient is zero
+    if (p.s_kv > 0) {
+      const long long rows = (long long)nbh * p.s_kv;
+      const int per = 256 / (D / 8);
+      const dim3 g((unsigned)((rows + per - 1) / per));
+      void* a1[] = {&arg.dk, &arg.dk_sb, &arg.dk_sh, &arg.dk_ss, &arg.b, &arg.h, &arg.s_kv};
+      e = hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a1, 0, stream);
+      if (e != hipSuccess) return e;
+      void* a2[] = {&arg.dv, &arg.dv_sb, &arg.dv_sh, &arg.dv_ss, &arg.b, &arg.h, &arg.s_kv};
+      return hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a2, 0, stream);
+    }
+    if (p.s_q > 0) {
+      const long long rows = (long long)nbh * p.s_q;
+      const int per = 256 / (D / 8);
+      const dim3 g((unsigned)((rows + per - 1) / per));
+      void* a1[] = {&arg.dq, &arg.dq_sb, &arg.dq_sh, &arg.dq_ss, &arg.b, &arg.h, &arg.s_q};
+      return hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a1, 0, stream);
+    }
+    return hipSuccess;
+  }
+  {
+    const int rpb = kPreThreads / (D / 8);
+    void* args[] = {&arg, &lse2};
+    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((n + rpb - 1) / rpb)),
+                        dim3(kPreThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  {
+    const long long g = (long long)nbh * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
+    void* args[] = {&arg, &lse2};
+    e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL>, dim3((unsigned)g),
+                        dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  {
+    const long long g = (long long)nbh * ((p.s_q + kDqRows - 1) / kDqRows);
+    void* args[] = {&arg, &lse2};
+    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL>, dim3((unsigned)g),
+                        dim3(kBwdThreads), args, 0, stream);
+  }
+  return e;
+}
+
+template <typename T, int D>
+hipError_t launch_d(const BwdParams& p, bool causal, hipStream_t stream) {
+  return causal ? launch_typed<T, D, true>(p, stream) : launch_typed<T, D, false>(p, stream);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(long long rows) {
+  // D (rows floats, padded to 64) then LSE in base 2 (rows floats)
+  const size_t n = (size_t)((rows + 63) / 64 * 64);
+  return ((2 * n * sizeof(float)) + 255) / 256 * 256;
+}
+
+hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream) {
+  if (dt == Dt::BF16)
+    return d == 64 ? launch_d<__bf16, 64>(p, causal, stream) : launch_d<__bf16, 128>(p, causal, stream);
+  if (dt == Dt::F16)
+    return d == 64 ? launch_d<_Float16, 64>(p, causal, stream)
+                   : launch_d<_Float16, 128>(p, causal, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace sdpa07

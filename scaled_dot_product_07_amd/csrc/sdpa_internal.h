@@ -44,7 +44,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: rowsum(dO * O), fp32 [b][h][s_q]
+  float* delta;  // workspace: rowsum(dO * O), fp32 [b][h][s_q]; then LSE * log2(e)
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -70,8 +70,12 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
 // Enqueue the three backward kernels; returns the first failing launch status.
 hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream);
 
-// Query tiles of the dK/dV and dQ passes (exported for grid sizing).
-constexpr int kBwdBlockM = 64;
-constexpr int kBwdBlockN = 64;
+// Bytes of backward workspace for `rows` = b * h * s_q query rows: the fp32
+// row dot products rowsum(dO * O) and the statistic in base 2.
+size_t bwd_workspace_bytes(long long rows);
+
+// Tile sizes of the dK/dV and dQ passes (for grid-size validation).
+constexpr int kBwdBlockM = 128;
+constexpr int kBwdBlockN = 128;
 
 }  // namespace sdpa07

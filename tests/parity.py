@@ -3,7 +3,9 @@
 Tolerances (written here once, used by every GPU test):
   O   : max|O - O_ref| <= 2e-2 * max|O_ref| for fp16/bf16 io, <= 1e-4 absolute for fp32 io
   LSE : max|LSE - LSE_ref| <= 5e-3 (natural log units), -inf exactly where the oracle has -inf
-  dQ, dK, dV : max|G - G_ref| <= 5e-2 * max|G_ref| per tensor
+  dQ, dK, dV : max|G - G_ref| <= 5e-2 * max|G_ref| per tensor, with an absolute
+               floor of 1e-5 for references that are identically zero (one visible
+               key: dS = dP - D vanishes exactly, the GPU leaves ~1e-7 of rounding)
 The reference is always the fp64 oracle run on the very same input bytes.
 """
 
@@ -18,6 +20,7 @@ O_REL_TOL = {"bf16": 2e-2, "fp16": 2e-2}
 O_ABS_TOL_FP32 = 1e-4
 LSE_ABS_TOL = 5e-3
 GRAD_REL_TOL = 5e-2
+GRAD_ABS_FLOOR = 1e-5
 
 DT_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
 
@@ -59,6 +62,6 @@ def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, what: str) -> float:
     assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite values"
     ref_max = float(np.max(np.abs(g_ref))) if g_ref.size else 0.0
     err = float(np.max(np.abs(g_gpu - g_ref))) if g_ref.size else 0.0
-    tol = GRAD_REL_TOL * ref_max
+    tol = max(GRAD_REL_TOL * ref_max, GRAD_ABS_FLOOR)
     assert err <= tol, f"{what}: max|diff| {err:.3e} > tol {tol:.3e}"
     return err

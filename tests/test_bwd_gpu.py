@@ -1,0 +1,122 @@
+"""GPU parity of the dense backward (sdpa_bwd) against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's O and LSE; the oracle runs its own
+fp64 forward. Tolerance per gradient tensor: max|G - G_ref| <= 5e-2 max|G_ref|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import announce, check_grad, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_bwd(q, k, v, do, scale, causal, dev, o=None, lse=None):
+    import scaled_dot_product_07_amd as sdpa
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    if o is None:
+        o, lse = sdpa.fwd(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = sdpa.bwd(qd, kd, vd, o.to(dev), dod, lse.to(dev), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SMALL = [
+    # dtype, b, h, s_q, s_kv, d, causal, layout
+    ("bf16", 1, 2, 200, 200, 64, True, "bhsd"),
+    ("bf16", 1, 2, 200, 200, 64, False, "bhsd"),
+    ("fp16", 1, 2, 257, 257, 128, True, "bhsd"),
+    ("fp16", 1, 2, 257, 257, 128, False, "bshd"),
+    ("bf16", 2, 2, 130, 190, 64, True, "bhsd"),
+    ("bf16", 1, 1, 190, 130, 128, True, "bshd"),
+    ("bf16", 1, 1, 1, 1, 64, True, "bhsd"),
+    ("bf16", 1, 3, 64, 300, 128, False, "bhsd"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_vs_oracle(gpu, case):
+    dt, b, h, sq, skv, d, causal, layout = case
+    announce(f"bwd small {case}")
+    q, k, v, do = W.dense_inputs(b, h, sq, skv, d, dt, layout, seed=11 + sq + d,
+                                 with_dout=True)
+    scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = _gpu_bwd(q, k, v, do, scale, causal, gpu)
+    _, _, dq_r, dk_r, dv_r = oracle.bwd(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    check_grad(f64(dq), dq_r, "dQ")
+    check_grad(f64(dk), dk_r, "dK")
+    check_grad(f64(dv), dv_r, "dV")
+    assert dq.stride() == q.stride() and dk.stride() == k.stride()
+
+
+def test_with_oracle_forward_outputs(gpu):
+    """Feed the oracle's O (cast to bf16) and LSE: isolates the backward's own error."""
+    announce("bwd with oracle O/LSE")
+    q, k, v, do = W.dense_inputs(1, 2, 300, 300, 128, "bf16", "bhsd", seed=21, with_dout=True)
+    scale = 0.1
+    o_r, lse_r, dq_r, dk_r, dv_r = oracle.bwd(f64(q), f64(k), f64(v), f64(do), scale, True)
+    o = torch.from_numpy(o_r).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_r).to(torch.float32)
+    dq, dk, dv = _gpu_bwd(q, k, v, do, scale, True, gpu, o=o, lse=lse)
+    check_grad(f64(dq), dq_r, "dQ")
+    check_grad(f64(dk), dk_r, "dK")
+    check_grad(f64(dv), dv_r, "dV")
+
+
+def test_negative_scale(gpu):
+    announce("bwd negative scale")
+    q, k, v, do = W.dense_inputs(1, 2, 150, 150, 64, "bf16", "bhsd", seed=23, with_dout=True)
+    dq, dk, dv = _gpu_bwd(q, k, v, do, -0.2, True, gpu)
+    _, _, dq_r, dk_r, dv_r = oracle.bwd(f64(q), f64(k), f64(v), f64(do), -0.2, True)
+    check_grad(f64(dq), dq_r, "dQ")
+    check_grad(f64(dk), dk_r, "dK")
+    check_grad(f64(dv), dv_r, "dV")
+
+
+def test_deterministic(gpu):
+    announce("bwd determinism")
+    q, k, v, do = W.dense_inputs(2, 4, 384, 384, 128, "bf16", "bhsd", seed=25, with_dout=True)
+    a = _gpu_bwd(q, k, v, do, 0.09, True, gpu)
+    b = _gpu_bwd(q, k, v, do, 0.09, True, gpu)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_empty_sides_give_zero_gradients(gpu):
+    import scaled_dot_product_07_amd as sdpa
+    announce("bwd empty sides")
+    q = torch.randn(1, 2, 70, 64, dtype=torch.bfloat16, device=gpu)
+    k0 = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=gpu)
+    lse = torch.full((1, 2, 70), float("-inf"), device=gpu)
+    dq = torch.full_like(q, 5.0)
+    dq, _, _ = sdpa.bwd(q, k0, k0, torch.zeros_like(q), q, lse, causal=False, dq=dq)
+    q0 = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=gpu)
+    k = torch.randn(1, 2, 50, 64, dtype=torch.bfloat16, device=gpu)
+    dk, dv = torch.full_like(k, 3.0), torch.full_like(k, 4.0)
+    _, dk, dv = sdpa.bwd(q0, k, k, q0, q0, torch.empty(1, 2, 0, device=gpu), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_workload_bwd_b4h16s2048d128_sampled(gpu):
+    """The backward workload at full size: two whole heads against the oracle,
+    plus identities on every head: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0."""
+    c = W.BWD_BF16_B4H16S2048D128
+    announce(c.name)
+    q, k, v, do = W.case_inputs(c)
+    dq, dk, dv = _gpu_bwd(q, k, v, do, c.scale, True, gpu)
+    for (bi, hi) in [(0, 0), (3, 15)]:
+        sl = lambda x: f64(x[bi:bi + 1, hi:hi + 1])  # noqa: E731
+        _, _, dq_r, dk_r, dv_r = oracle.bwd(sl(q), sl(k), sl(v), sl(do), c.scale, True)
+        check_grad(sl(dq), dq_r, f"dQ[b{bi},h{hi}]")
+        check_grad(sl(dk), dk_r, f"dK[b{bi},h{hi}]")
+        check_grad(sl(dv), dv_r, f"dV[b{bi},h{hi}]")
+    dv_sum = dv.double().sum(2)
+    do_sum = do.to(gpu).double().sum(2)
+    assert torch.max(torch.abs(dv_sum - do_sum)) <= 5e-2 * torch.max(torch.abs(do_sum))
+    dk_sum = dk.double().sum(2)
+    assert torch.max(torch.abs(dk_sum)) <= 5e-2 * torch.max(torch.abs(dk.double()))
