@@ -46,6 +46,57 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16s1024d64_causal_
 FWD_SOURCE = os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", "fwd.hip")
 
 
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+FWD_KERNEL_TAG = "fwd16_kernel"
+
+
+def _pmc_means(root, counter):
+    """Mean counter value per dispatch for the forward kernel and for the copy kernel."""
+    import csv
+    import glob
+    fwd, cp = [], []
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            name, val = row["Kernel_Name"], float(row["Counter_Value"])
+            if FWD_KERNEL_TAG in name and "DF16b" in name and "Li64ELb1ELb0" in name:
+                fwd.append(val)
+            elif "copy" in name.lower() and "fill" not in name.lower():
+                cp.append(val)
+    if not fwd or not cp:
+        raise SystemExit(f"{root}: {counter} rows missing (fwd {len(fwd)}, copy {len(cp)})")
+    return sum(fwd) / len(fwd), sum(cp) / len(cp), len(fwd)
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the headline forward, each
+    scaled by bytes / counter of a plain copy of COPY_BYTES, written next to the
+    forward's source digest (a summary taken on other source is not used)."""
+    f_fwd, f_cp, n_f = _pmc_means(fetch_dir, "FETCH_SIZE")
+    w_fwd, w_cp, n_w = _pmc_means(write_dir, "WRITE_SIZE")
+    kf = COPY_BYTES / (f_cp * 1024.0)
+    kw = COPY_BYTES / (w_cp * 1024.0)
+    read_b = f_fwd * 1024.0 * kf
+    write_b = w_fwd * 1024.0 * kw
+    out = {
+        "kernel": "fwd16_kernel<bf16, d64, causal, dense>",
+        "workload": "b4 h16 s1024 d64 causal bf16 BHSD",
+        "fwd_source_sha256_16": source_digest(FWD_SOURCE),
+        "fetch_kib_per_dispatch": f_fwd, "write_kib_per_dispatch": w_fwd,
+        "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "copy_bytes": COPY_BYTES,
+        "fetch_scale": kf, "write_scale": kw,
+        "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": read_b + write_b,
+        "algorithmic_bytes_per_launch": 4 * 4 * 16 * 1024 * 64 * 2 + 4 * 16 * 1024 * 4,
+        "dispatches": [n_f, n_w],
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_SUMMARY), exist_ok=True)
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def fwd_flops(b, h, s_q, s_kv, d, causal):
     f = 4.0 * b * h * s_q * s_kv * d
     return f * 0.5 if causal else f
@@ -145,7 +196,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of one graph replay (for profilers)")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a plain device copy of COPY_BYTES (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
+                         "with --copy-calibrate into the HBM traffic summary, then exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -199,6 +258,12 @@ def main():
         result["cpu_baseline"] = cpu_baseline(q, k, v, c.scale, c.causal, flops)
     if extra:
         result["extra"] = extra
+    if args.copy_calibrate:
+        src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result), flush=True)
 
 
