@@ -70,6 +70,17 @@ sdpa_status check_tensor(const char* name, const void* ptr, const int64_t* st, c
   return SDPA_OK;
 }
 
+// Key rows are streamed in tiles addressed with 32-bit byte offsets from the
+// tile's first row: a tile of kTileRows rows must span less than 2 GiB.
+sdpa_status check_tile_span(const char* name, int64_t row_stride, sdpa_dtype dt) {
+  constexpr int64_t kTileRows = 128;
+  const int64_t span = (row_stride < 0 ? -row_stride : row_stride) * elem_size(dt) * kTileRows;
+  if (span >= 0x7fffffffLL)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: row stride %lld too large for 32-bit tile offsets", name,
+                (long long)row_stride);
+  return SDPA_OK;
+}
+
 sdpa07::Dt to_dt(sdpa_dtype dt) {
   return dt == SDPA_FP32 ? sdpa07::Dt::F32 : dt == SDPA_FP16 ? sdpa07::Dt::F16 : sdpa07::Dt::BF16;
 }
@@ -124,6 +135,8 @@ sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float
   if ((st = check_tensor("v", v, v_stride, ks, 4, dtype, work && s_kv > 0)) != SDPA_OK) return st;
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
+  if ((st = check_tile_span("k", k_stride[2], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("v", v_stride[2], dtype)) != SDPA_OK) return st;
   const long long n_qtiles = (s_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
   if ((long long)b * h * n_qtiles > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid of %lld workgroups exceeds int32",
@@ -180,6 +193,8 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
     return st;
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
+  if ((st = check_tile_span("k", k_stride[0], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("v", v_stride[0], dtype)) != SDPA_OK) return st;
   const long long n_qtiles = (max_seqlen_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
   if ((long long)num_seqs * h * n_qtiles > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");

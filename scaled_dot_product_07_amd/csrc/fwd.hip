@@ -129,6 +129,14 @@ __device__ __forceinline__ int s_key(int mb, int r, int hf) {
   return 32 * mb + 8 * (r / 4) + 4 * hf + (r % 4);
 }
 
+// Masks every score of a tile (a neutralised softmax).
+__device__ __forceinline__ void mask_all(f32x16 (&s)[2]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mb][r] = -INFINITY;
+}
+
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len,
                                           int hf) {
@@ -248,30 +256,35 @@ fwd16_kernel(FwdParams p) {
   float l_run = 0.f;
   const float c = p.scale_log2;
 
-  // K/V tile loads through a buffer resource rebased per tile: rows at or
-  // past the sequence's key count get an out-of-range offset and read as
-  // zeros, without a branch (and without touching memory past the keys).
-  int kroff[CPT], vroff[CPT], lrow[CPT];
+  // K/V tile loads through a buffer resource rebased per tile whose byte
+  // bound ends with the last key row of the sequence: loads of rows past it
+  // read as zeros (rows are disjoint when the row stride is at least d, which
+  // every dense layout satisfies; with overlapping rows the extra rows are
+  // real, finite keys that the mask hides), with no per-lane test and no
+  // memory touched past the keys.
+  int kroff[CPT], vroff[CPT];
 #pragma unroll
   for (int x = 0; x < CPT; ++x) {
     const int ch = tid + NT * x;
-    lrow[x] = ch / CH_ROW;
-    const int cc = ch % CH_ROW;
-    kroff[x] = lrow[x] * (int)p.k_ss * (int)sizeof(T) + cc * 16;
-    vroff[x] = lrow[x] * (int)p.v_ss * (int)sizeof(T) + cc * 16;
+    const int r = ch / CH_ROW, cc = ch % CH_ROW;
+    kroff[x] = r * (int)p.k_ss * (int)sizeof(T) + cc * 16;
+    vroff[x] = r * (int)p.v_ss * (int)sizeof(T) + cc * 16;
   }
-  i16x8 kreg[CPT], vreg[CPT];
+  // K/V tiles are staged through registers PD tiles ahead of their LDS store
+  // (two stages where registers allow), so global latency is covered by PD
+  // pipeline steps
+  constexpr int PD = D <= 64 ? 2 : 1;
+  i16x8 kreg[PD][CPT], vreg[PD][CPT];
   auto gload = [&](i16x8(&reg)[CPT], const T* __restrict__ base, int64_t stride,
                    const int(&roff)[CPT], int j) {
     const T* tb = base + (int64_t)j * BN * stride;
-    const int rows = kv_len - j * BN;
+    const int rows = min(kv_len - j * BN, BN);
+    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, 0x7fffffff, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, kBufferFlags);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int off = lrow[x] < rows ? roff[x] : kOutOfRange;
-      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    }
+    for (int x = 0; x < CPT; ++x)
+      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, roff[x], 0, 0));
   };
   auto lstore = [&](T* buf, const i16x8(&reg)[CPT]) {
 #pragma unroll
@@ -418,22 +431,27 @@ fwd16_kernel(FwdParams p) {
   // makes the softmax a no-op (P = 0), and an unneeded QK only computes a
   // value that is never used. A wave skips the tiles past its causal range
   // (j > wave_tiles) except for the memory work the whole workgroup shares.
-  auto step = [&](int j, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
-                  v8(&p_cur)[4]) {
-    // K_{j+1} into LDS (its global load was issued one block ago); the
-    // loads and stores run unconditionally so that wait counts stay exact (a
-    // load past the keys reads zeros through the buffer bound)
-    lstore(kl[(j + 1) & 1], kreg);
+  // `par` is j mod 2, known at compile time (the loop is unrolled by two)
+  auto step = [&](int j, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+                  const v8(&p_prev)[4], v8(&p_cur)[4]) {
+    constexpr int J = decltype(par)::value;
+    constexpr int KS = (J + 1) % PD, VS = J % PD;  // register stages of K_{j+1}, V_j
+    // K_{j+1} into LDS (its global load was issued PD blocks ago); the loads
+    // and stores run unconditionally so that wait counts stay exact (a load
+    // past the keys reads zeros through the buffer bound)
+    lstore(kl[(j + 1) & 1], kreg[KS]);
     __syncthreads();
-    lstore(vl[j & 1], vreg);
-    gload(vreg, V, p.v_ss, vroff, j + 1);
-    gload(kreg, K, p.k_ss, kroff, j + 2);
+    lstore(vl[j & 1], vreg[VS]);
+    gload(vreg[VS], V, p.v_ss, vroff, j + PD);
+    gload(kreg[KS], K, p.k_ss, kroff, j + 1 + PD);
     if (j <= wave_tiles) {
       const int kbase = j * BN;
-      // keys at or past kv_lim are masked: all of them once the wave is past its range
-      const int kv_lim = j < wave_tiles ? kv_len : 0;
-      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_lim) {
-        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_lim, hf);
+      if (j == wave_tiles) {
+        mask_all(s_cur);  // past this wave's range: a neutralised softmax
+        m_cur = m_prev;
+        a_cur = 1.f;
+      } else if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_len) {
+        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf);
         offset_update(row_max(s_cur), m_prev, m_cur, a_cur);  // redo with the mask
       }
       const bool rescale = __any(a_cur != 1.f);
@@ -454,26 +472,30 @@ fwd16_kernel(FwdParams p) {
       pa[t] = v8{};
       pb[t] = v8{};
     }
-    gload(kreg, K, p.k_ss, kroff, 0);
-    gload(vreg, V, p.v_ss, vroff, 0);
-    lstore(kl[0], kreg);
+    gload(kreg[0], K, p.k_ss, kroff, 0);
+#pragma unroll
+    for (int t = 0; t < PD; ++t) gload(vreg[t], V, p.v_ss, vroff, t);
+    lstore(kl[0], kreg[0]);
     {
       const i16x8 zero[CPT] = {};
       lstore(vl[1], zero);  // read by the no-op P.V of the first block
     }
-    gload(kreg, K, p.k_ss, kroff, 1);
+#pragma unroll
+    for (int t = 1; t <= PD; ++t) gload(kreg[t % PD], K, p.k_ss, kroff, t);
     __syncthreads();
     // S_0 = QK(K_0) and its offset; the P.V and softmax parts are neutralised
     // (sb fully masked, P_{-1} = 0, V buffer 1 zero)
-    mask_tile<CAUSAL>(sb, 0, qi, 0, hf);
+    mask_all(sb);
     block(kl[0], vl[1], sb, sa, pb, pa);
     int j = 0;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     for (; j + 1 < n_tiles; j += 2) {
-      step(j, sa, sb, pb, pa);
-      step(j + 1, sb, sa, pa, pb);
+      step(j, I0{}, sa, sb, pb, pa);
+      step(j + 1, I1{}, sb, sa, pa, pb);
     }
     if (j < n_tiles) {
-      step(j, sa, sb, pb, pa);
+      step(j, I0{}, sa, sb, pb, pa);
       ++j;
     }
     // drain: P.V of the last tile, whose V was stored in the last block; the
@@ -484,10 +506,10 @@ fwd16_kernel(FwdParams p) {
       m_cur = m_l;
       a_cur = 1.f;
       if ((j - 1) & 1) {
-        mask_tile<CAUSAL>(sa, 0, qi, 0, hf);
+        mask_all(sa);
         block(kl[0], vl[1], sa, sb, pb, pa);
       } else {
-        mask_tile<CAUSAL>(sb, 0, qi, 0, hf);
+        mask_all(sb);
         block(kl[0], vl[0], sb, sa, pa, pb);
       }
     }

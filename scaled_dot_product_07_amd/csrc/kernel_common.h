@@ -48,12 +48,13 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Pins the computation of x to this point of the instruction stream (an empty
-// volatile asm that "modifies" x: its producers are emitted before it and its
-// users after it). Used to keep softmax work interleaved with MFMAs.
+// Pins the computation of x before this point of the instruction stream (an
+// empty volatile asm that reads x: volatile asms keep their order, so x's
+// producers cannot sink past it). Used to keep softmax work interleaved with
+// the MFMAs it is meant to overlap.
 template <typename X>
-__device__ __forceinline__ void pin(X& x) {
-  asm volatile("" : "+v"(x));
+__device__ __forceinline__ void pin(const X& x) {
+  asm volatile("" ::"v"(x));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
