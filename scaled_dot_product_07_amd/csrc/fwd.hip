@@ -240,16 +240,8 @@ fwd16_kernel(FwdParams p) {
       !wave_active ? 0 : (CAUSAL ? min(kv_len, min(q_len, row0 + 32)) : kv_len);
   const int wave_tiles = (wave_kv_end + BN - 1) / BN;
 
-  // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7].
   v8 qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    i16x8 raw = {};
-    if (q_valid) raw = *(const i16x8*)(Q + (int64_t)qi * p.q_ss + 16 * ks + 8 * hf);
-    if (p.negate_q) raw ^= (short)0x8000;
-    qf[ks] = __builtin_bit_cast(v8, raw);
-  }
-
+  i16x8 qraw[D / 16];
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
@@ -475,6 +467,25 @@ fwd16_kernel(FwdParams p) {
     gload(kreg[0], K, p.k_ss, kroff, 0);
 #pragma unroll
     for (int t = 0; t < PD; ++t) gload(vreg[t], V, p.v_ss, vroff, t);
+    // Q rows as B operands of S^T = K Q^T (lane holds Q[qi][16ks + 8hf .. +7]),
+    // loaded after the first K/V tiles are requested so that the two
+    // latencies overlap; rows past the sequence read as zeros
+    {
+      const T* qb = Q + (int64_t)(qt * BM) * p.q_ss;
+      const int rows = min(q_len - qt * BM, BM);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)qb, (short)0, ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T), kBufferFlags);
+      const int qoff = (qi - qt * BM) * (int)p.q_ss * (int)sizeof(T) + 16 * hf;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        qraw[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, qoff + 32 * ks, 0, 0));
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      i16x8 raw = qraw[ks];
+      if (p.negate_q) raw ^= (short)0x8000;
+      qf[ks] = __builtin_bit_cast(v8, raw);
+    }
     lstore(kl[0], kreg[0]);
     {
       const i16x8 zero[CPT] = {};
