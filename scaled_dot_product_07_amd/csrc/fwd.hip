@@ -152,45 +152,62 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int
 // ---------------------------------------------------------------------------
 // fp16 / bf16 io.
 //
-// A workgroup of 8 waves owns a PAIR of 128-row query tiles of one head: tile
-// i (waves 0-3) and tile n-1-i (waves 4-7). Under the causal mask their key
-// counts sum to the same total for every pair, so every workgroup (and every
-// SIMD, which runs one wave of each tile) gets the same work; the key tiles
-// the short tile needs are a prefix of the long tile's and are loaded once.
+// A workgroup of 8 waves owns one 128-row query tile of one (b|sequence, h).
+// Waves w and w+4 sit on the same SIMD and own the same 32 query rows; they
+// split the keys: key tile t belongs to wave group t % 2. Both waves of a SIMD
+// therefore get the same work (a causal tile's keys are split evenly), each
+// hides the other's waits, and one barrier serves two key tiles. At the end
+// the two partial results of a row group, (O, offset, l), are merged through
+// LDS. Query tiles are ordered heaviest first so that the hardware's dynamic
+// dispatch of workgroups to CUs balances the causal work (longest first).
 //
-// Per wave and key tile the work is software-pipelined: the QK^T products of
-// tile j+1 are issued in the same basic block as the softmax of tile j, so
-// the exp/convert/max VALU work fills the MFMA pipeline's issue gaps; the
-// P.V products of tile j then overlap the row sums. The running max used as
-// the exponent offset is only raised when a tile's max exceeds it by more
-// than kTau (log2 units), so P <= 2^kTau and the O accumulator is rescaled
-// only on those (rare) tiles; the result is exact either way because O and l
-// always share the same offset.
+// Step s of the key loop is one barrier and one straight-line block per wave
+// (see `block`): the QK^T products of the wave's tile of step s+1, the P.V
+// products of its tile of step s-1 and the softmax of its tile of step s,
+// with the workgroup's share of the LDS stores of K(s+2) and V(s) and of the
+// global loads of later tiles spread over the block.
+//
+// Softmax offsets are lazy: the offset m of a row (log2 units) is raised
+// only when a tile's max exceeds it by more than kTau, so P <= 2^kTau and the
+// O accumulator is rescaled only on those (rare) tiles; the result is exact
+// either way because O and l always share the same offset. The decision is
+// taken between blocks, from the row max that the previous block computed.
+// The scale stays in fp32 (P = 2^(c*S - m), one fma per score): folding it
+// into Q would round c*Q to the io type and shift scores by up to 2^-9 of
+// their size.
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kFwdThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
-  constexpr int NT = kFwdThreads16;
-  constexpr int PITCH = D + 8;  // LDS row pitch (elements); +16 B breaks bank aliasing
-  constexpr int CH_ROW = D / 8;  // 16-byte chunks per row
-  constexpr int CPT = BN * CH_ROW / NT;  // chunks per thread per tensor per tile
-  static_assert(CPT >= 1, "tile too small for the workgroup");
+  constexpr int NT = kFwdThreads16;   // 8 waves
+  // Row pitches (elements). K: +16 B, so the 16 lanes of a ds_read_b128
+  // phase (16 rows) hit distinct banks. V: row stride = 64 B mod 256 B, so
+  // the four 64-byte row pieces that a transposing read covers per 32 lanes
+  // hit distinct banks.
+  constexpr int KP = D + 8;
+  constexpr int VP = D + 32;
+  constexpr int CH_ROW = D / 8;       // 16-byte chunks per row
+  constexpr int TILE_CH = BN * CH_ROW;
+  constexpr int CPT = 2 * TILE_CH / NT;  // chunks per thread per tensor per step (two tiles)
+  static_assert(CPT >= 1 && (2 * TILE_CH) % NT == 0, "tile/workgroup mismatch");
+  // chunk x of a thread lies in tile NT*x / TILE_CH for every thread, so each
+  // buffer resource is uniform over the wave
+  static_assert(TILE_CH % NT == 0, "a thread's chunk must not straddle tiles");
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  __shared__ __attribute__((aligned(16))) T kl[2][BN * PITCH];
-  __shared__ __attribute__((aligned(16))) T vl[2][BN * PITCH];
+  // [buffer][key group][tile]
+  __shared__ __attribute__((aligned(16))) T kl[2][2][BN * KP];
+  __shared__ __attribute__((aligned(16))) T vl[2][2][BN * VP];
 
-  // ---- work unit: (query tile, b|sequence, h). Query tiles are ordered as a
-  // snake, heaviest causal tile first: n-1, n-2, .., n/2, then 0, 1, .., so the
-  // two workgroups resident on a CU (dispatched nbh*ceil(n/2) apart) pair a
-  // heavy tile with a light one.
+  // ---- work unit: causal, a pair of query tiles (n-1-i, i) of one
+  // (b|sequence, h), the heavier first, so that every pair holds the same
+  // causal work; otherwise one query tile (all tiles cost the same)
   const int nbh = p.b * p.h;
-  const int urow = blockIdx.x / nbh;
+  const int pair = (int)(blockIdx.x / nbh);
+  constexpr int PASSES = CAUSAL ? 2 : 1;
   const int bh = blockIdx.x % nbh;
-  const int half = (p.n_qtiles + 1) / 2;
-  const int qt_sched = urow < half ? p.n_qtiles - 1 - urow : urow - half;
   const int bi = bh / p.h, hi = bh % p.h;
   int q_len, kv_len;
   int64_t q_off, k_off, v_off, o_off, lse_off, lse_st;
@@ -217,8 +234,6 @@ fwd16_kernel(FwdParams p) {
     lse_off = ((int64_t)bi * p.h + hi) * p.s_q;
     lse_st = 1;
   }
-  if (qt_sched * BM >= q_len) return;  // uniform over the workgroup, before any barrier
-
   const T* __restrict__ Q = (const T*)p.q + q_off;
   const T* __restrict__ K = (const T*)p.k + k_off;
   const T* __restrict__ V = (const T*)p.v + v_off;
@@ -227,79 +242,84 @@ fwd16_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid % 64;
   // wave-uniform values live in SGPRs so per-wave control flow stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int g = wave / 4;       // key group: key tiles g, g+2, g+4, ...
+  const int rg = wave % 4;      // row group
   const int hf = lane / 32, col = lane % 32;
-  const int qt = qt_sched;
-  const int row0 = qt * BM + wave * 32;
-  const int qi = row0 + col;
+
+  for (int pass = 0; pass < PASSES; ++pass) {
+  const int qt = !CAUSAL ? pair : pass == 0 ? p.n_qtiles - 1 - pair : pair;
+  if (pass == 1 && qt >= p.n_qtiles - 1 - pair) break;  // odd count: middle tile alone
+  if (qt * BM >= q_len) continue;  // uniform over the workgroup
+  if (pass == 1) __syncthreads();  // the first tile's epilogue is done with LDS
+  const int row0 = qt * BM + rg * 32;  // first query row of this wave
+  const int qi = row0 + col;           // this lane's query row
   const bool wave_active = row0 < q_len;
   const bool q_valid = wave_active && qi < q_len;
   const int last_q = min(q_len, (qt + 1) * BM) - 1;
   const int kv_end = CAUSAL ? min(kv_len, last_q + 1) : kv_len;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  const int n_steps = (n_tiles + 1) / 2;  // two key tiles per step
   const int wave_kv_end =
       !wave_active ? 0 : (CAUSAL ? min(kv_len, min(q_len, row0 + 32)) : kv_len);
-  const int wave_tiles = (wave_kv_end + BN - 1) / BN;
+  const int wave_tiles_all = (wave_kv_end + BN - 1) / BN;
+  // steps in which this wave has a key tile of its own (tile 2s + g)
+  const int wave_steps = wave_tiles_all > g ? (wave_tiles_all - g + 1) / 2 : 0;
 
   v8 qf[D / 16];
-  i16x8 qraw[D / 16];
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float l_run = 0.f;
   const float c = p.scale_log2;
 
-  // K/V tile loads through a buffer resource rebased per tile whose byte
-  // bound ends with the last key row of the sequence: loads of rows past it
-  // read as zeros (rows are disjoint when the row stride is at least d, which
-  // every dense layout satisfies; with overlapping rows the extra rows are
-  // real, finite keys that the mask hides), with no per-lane test and no
-  // memory touched past the keys.
-  int kroff[CPT], vroff[CPT];
-#pragma unroll
-  for (int x = 0; x < CPT; ++x) {
-    const int ch = tid + NT * x;
-    const int r = ch / CH_ROW, cc = ch % CH_ROW;
-    kroff[x] = r * (int)p.k_ss * (int)sizeof(T) + cc * 16;
-    vroff[x] = r * (int)p.v_ss * (int)sizeof(T) + cc * 16;
-  }
-  // K/V tiles are staged through registers PD tiles ahead of their LDS store
-  // (two stages where registers allow), so global latency is covered by PD
-  // pipeline steps
+  // K/V loads: each step the workgroup loads tiles 2s (group 0) and 2s + 1
+  // (group 1), through a buffer resource rebased per tile whose byte bound
+  // ends with the last key row any query of the tile sees (kv_end): rows past
+  // it read as zeros and are masked anyway (rows are disjoint when the row
+  // stride is at least d, which every dense layout satisfies; with
+  // overlapping rows the extra rows are real, finite keys that the mask
+  // hides), with no per-lane test and no memory touched past the keys.
+  // Chunk x of thread tid is row tid / CH_ROW + XROW(x) of tile XT(x), 16
+  // bytes at column (tid % CH_ROW) * 8; the per-x parts are uniform (a
+  // scalar offset of the buffer load) or constant (an LDS immediate).
+  auto XT = [](int x) { return NT * x / TILE_CH; };
+  auto XROW = [](int x) { return (NT * x % TILE_CH) / CH_ROW; };
+  const int kroff = (tid / CH_ROW) * (int)p.k_ss * (int)sizeof(T) + (tid % CH_ROW) * 16;
+  const int vroff = (tid / CH_ROW) * (int)p.v_ss * (int)sizeof(T) + (tid % CH_ROW) * 16;
+  const int kldso = (tid / CH_ROW) * KP + (tid % CH_ROW) * 8;
+  const int vldso = (tid / CH_ROW) * VP + (tid % CH_ROW) * 8;
+  // buffer resource of key tile t (zero bytes for tiles outside the keys);
+  // built in scalar code outside the fused blocks
+  auto tile_rsrc = [&](const T* __restrict__ base, int64_t stride,
+                       int t) -> __amdgpu_buffer_rsrc_t {
+    const T* tb = base + (int64_t)t * BN * stride;
+    const int rows = t < 0 ? 0 : min(kv_end - t * BN, BN);
+    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, kBufferFlags);
+  };
+  auto gload = [&](__amdgpu_buffer_rsrc_t rs, int voff, int soff) -> i16x8 {
+    return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+  };
+  auto kload = [&](const __amdgpu_buffer_rsrc_t(&r2)[2], int x) -> i16x8 {
+    return gload(r2[XT(x)], kroff, XROW(x) * (int)p.k_ss * (int)sizeof(T));
+  };
+  auto vload = [&](const __amdgpu_buffer_rsrc_t(&r2)[2], int x) -> i16x8 {
+    return gload(r2[XT(x)], vroff, XROW(x) * (int)p.v_ss * (int)sizeof(T));
+  };
+  auto kslot = [&](int x) { return XT(x) * BN * KP + XROW(x) * KP + kldso; };
+  auto vslot = [&](int x) { return XT(x) * BN * VP + XROW(x) * VP + vldso; };
+  // register stages between a tile's global load and its LDS store: the loads
+  // of K(s+2+PD) and V(s+PD) are issued in the block that stores K(s+2), V(s)
   constexpr int PD = D <= 64 ? 2 : 1;
   i16x8 kreg[PD][CPT], vreg[PD][CPT];
-  auto gload = [&](i16x8(&reg)[CPT], const T* __restrict__ base, int64_t stride,
-                   const int(&roff)[CPT], int j) {
-    const T* tb = base + (int64_t)j * BN * stride;
-    const int rows = min(kv_len - j * BN, BN);
-    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, kBufferFlags);
-#pragma unroll
-    for (int x = 0; x < CPT; ++x)
-      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, roff[x], 0, 0));
-  };
-  auto lstore = [&](T* buf, const i16x8(&reg)[CPT]) {
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + NT * x;
-      const int r = ch / CH_ROW, cc = ch % CH_ROW;
-      *(i16x8*)&buf[r * PITCH + cc * 8] = reg[x];
-    }
-  };
-  // Softmax state (per lane = per query row, both halves agree):
-  //   m_cur  offset of P_j (log2 units) for the tile the next block exponentiates
-  //   a_cur  2^(m_prev - m_cur): factor for l (in that block) and for O (after it)
-  //   m_prev offset of the previous tile (kept to redo the update after a mask)
-  //   m_l    offset of l (and of O once the pending P.V is added): the LSE base
-  float m_prev = -INFINITY, m_cur = -INFINITY, a_cur = 0.f, m_l = -INFINITY;
-  // lazy offset update from a tile max (raw score units): raise the offset
-  // only when the tile's max exceeds it by more than kTau
-  auto offset_update = [&](float mx, float m_from, float& m_to, float& a) {
-    const float mt = mx * c;
-    const float m_new = mt > m_from + kTau ? mt : m_from;
-    a = fast_exp2(m_from - (m_new == -INFINITY ? 0.f : m_new));
-    m_to = m_new;
-  };
+
+  // Softmax state (per lane = per query row; both halves agree):
+  //   m_cur  offset (log2 units) of the P that the next block computes; after
+  //          that block, also the offset of l and of O
+  //   a_cur  factor for l (in the block) and for O (after it) when the
+  //          offset was raised before the block, else 1
+  //   mx_nxt row max of the raw scores S the last block produced
+  float m_cur = -INFINITY, a_cur = 1.f, mx_nxt = -INFINITY;
   auto row_max = [&](const f32x16(&sv)[2]) -> float {
     float a = fmaxf(sv[0][0], sv[0][1]), b = fmaxf(sv[1][0], sv[1][1]);
 #pragma unroll
@@ -310,42 +330,96 @@ fwd16_kernel(FwdParams p) {
     const float mx = fmaxf(a, b);
     return fmaxf(mx, other_half(mx));
   };
+  // Offset decision for the coming block's scores, given their raw row max
+  // mx. Returns true (wave-uniform) when some row raised its offset; then
+  // a_cur holds the factor 2^(m_old - m_new) for those rows (1 elsewhere).
+  auto decide = [&](float mx) -> bool {
+    const float mt = mx * c;  // log2 units
+    const bool need = m_cur == -INFINITY ? mt != -INFINITY : mt > m_cur + kTau;
+    a_cur = 1.f;
+    if (!__any(need)) return false;
+    const float m_new = need ? mt : m_cur;
+    a_cur = need ? fast_exp2(m_cur - m_new) : 1.f;  // 0 for a row's first offset
+    m_cur = m_new;
+    return true;
+  };
 
-  // One pipeline block for key tile j of this wave, straight-line code:
-  //   QK  : S_{j+1} = K_{j+1} Q^T                (MFMAs 0 .. NQK-1)
-  //   PV  : O^T += V_{j-1}^T P_{j-1}^T             (MFMAs NQK .. NM-1)
-  //   SM  : P_j = 2^(c S_j - m_cur), row sum into l (VALU, early chunks)
-  //   MX  : row max of S_{j+1} and the next offset (VALU, last chunks, once
-  //         the QK results are complete)
+  // One pipeline block of step s, straight-line code:
+  //   QK  : S_next = K_next Q^T                  (MFMAs 0 .. NQK-1)
+  //   PV  : O^T += V_prev^T P_prev^T             (MFMAs NQK .. NM-1)
+  //   SM  : P_cur = 2^(scores), row sum into l   (VALU, early chunks)
+  //   MX  : row max of S_next                    (VALU, last chunks, once the
+  //                                               QK results are complete)
+  //   MEM : this thread's LDS stores of K(s+2) and V(s) and global loads of
+  //         K(s+2+PD) and V(s+PD), one instruction per chunk
   // It is emitted as NM chunks, each = the LDS read for the MFMA PF chunks
-  // ahead, one MFMA, and a slice of the VALU work; the slices are pinned to
-  // their chunk so the VALU work issues while the MFMA pipe is busy.
+  // ahead, one MFMA, a slice of the VALU work and at most one memory op; the
+  // slices are pinned to their chunk so the VALU work issues while the MFMA
+  // pipe is busy.
   constexpr int NQK = 2 * (D / 16);
   constexpr int NPV = 4 * (D / 32);
   constexpr int NM = NQK + NPV;
-  constexpr int PF = 3;                                   // LDS read-ahead (chunks)
+  constexpr int PF = D <= 64 ? 3 : 2;                     // LDS read-ahead (chunks)
   constexpr int NPAIR = 16;                               // 32 scores per lane, in pairs
   constexpr int EXP_CHUNKS = NM - 6 < 16 ? NM - 6 : 16;   // chunks holding the exps
-  constexpr int MX0 = NM - 4;                             // chunks MX0 .. MX0+2: max of S_{j+1}
+  constexpr int MX0 = NM - 4;                             // chunks MX0 .. MX0+2: max of S_next
+  constexpr int MEM0 = 1;                                 // chunks MEM0 .. MEM0+4*CPT-1
+  static_assert(MEM0 + 4 * CPT <= NM, "not enough chunks for the memory ops");
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
-  auto block = [&](const T* kb, const T* vb, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
-                   const v8(&p_prev)[4], v8(&p_cur)[4]) {
+  // MFMA A operands: K rows 32mb + col, d 16ks + 8hf .. +7 (S^T = K Q^T), and
+  // V^T rows (d) 32db + col for keys 16t + 8(e/4) + 4hf + e%4 (O^T = V^T P^T)
+  auto read_k = [&](const T* kb, int ks, int mb) -> v8 {
+    return *(const v8*)&kb[(32 * mb + col) * KP + 16 * ks + 8 * hf];
+  };
+  auto read_v = [&](const T* vb, int t, int db) -> v8 {
+    const T* a0 = vb + (16 * t + vrow) * VP + 32 * db + vcol;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(a0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(a0 + 8 * VP));
+    return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // S of the first step alone (its P.V and softmax have nothing to do)
+  auto qk_only = [&](const T* kb, f32x16(&s_out)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s_out[mb] = M::mma(read_k(kb, ks, mb), qf[ks], ks == 0 ? f32x16{} : s_out[mb]);
+    mx_nxt = row_max(s_out);
+  };
+  // the last P.V alone (after the last step)
+  auto pv_only = [&](const T* vb, const v8(&p_last)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
+  };
+  auto block = [&](int s, auto par, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+                   const v8(&p_prev)[4], v8(&p_cur)[4], const __amdgpu_buffer_rsrc_t(&rk)[2],
+                   const __amdgpu_buffer_rsrc_t(&rv)[2]) {
+    constexpr int R = decltype(par)::value % PD;  // register stage of K(s+2) and V(s)
+    const T* kb = kl[(s + 1) & 1][g];  // K of step s+1
+    const T* vb = vl[(s + 1) & 1][g];  // V of step s-1
+    T* kw = kl[s & 1][0];              // K(s+2), both tiles
+    T* vw = vl[s & 1][0];              // V(s), both tiles
     auto read_op = [&](int i) -> v8 {
-      if (i < NQK) {
-        const int ks = i / 2, mb = i % 2;
-        return *(const v8*)&kb[(32 * mb + col) * PITCH + 16 * ks + 8 * hf];
+      if (i < NQK) return read_k(kb, i / 2, i % 2);
+      return read_v(vb, (i - NQK) / (D / 32), (i - NQK) % (D / 32));
+    };
+    auto mem = [&](int i) {
+      const int k = i - MEM0;
+      if (k < 0 || k >= 4 * CPT) return;
+      const int x = k % CPT;
+      switch (k / CPT) {
+        case 0: *(i16x8*)&kw[kslot(x)] = kreg[R][x]; break;
+        case 1: *(i16x8*)&vw[vslot(x)] = vreg[R][x]; break;
+        case 2: kreg[R][x] = kload(rk, x); break;
+        default: vreg[R][x] = vload(rv, x); break;
       }
-      const int t = (i - NQK) / (D / 32), db = (i - NQK) % (D / 32);
-      const T* a0 = vb + (16 * t + vrow) * PITCH + 32 * db + vcol;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(a0));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(a0 + 8 * PITCH));
-      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
-    m_l = m_cur;
     float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
     i32x4 pk[4];
     auto slice = [&](int i) {
@@ -354,10 +428,11 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
         for (int pp = p0; pp < p1; ++pp) {
           const int t = pp / 4, e2 = pp % 4;
-          const f32x2 x = {fast_exp2(fmaf(s_cur[t / 2][8 * (t % 2) + 2 * e2], c, -m_off)),
-                           fast_exp2(fmaf(s_cur[t / 2][8 * (t % 2) + 2 * e2 + 1], c, -m_off))};
+          const float s0 = s_cur[t / 2][8 * (t % 2) + 2 * e2];
+          const float s1 = s_cur[t / 2][8 * (t % 2) + 2 * e2 + 1];
+          const f32x2 x = {fast_exp2(fmaf(s0, c, -m_off)), fast_exp2(fmaf(s1, c, -m_off))};
           const auto h = __builtin_convertvector(x, typename Pack2<T>::type);
-          int hb = __builtin_bit_cast(int, h);
+          const int hb = __builtin_bit_cast(int, h);
           pin(hb);
           pk[t][e2] = hb;
           if (e2 & 1) r1 = dot2_ones<T>(h, r1);
@@ -369,32 +444,30 @@ fwd16_kernel(FwdParams p) {
         pin(l_run);
       }
       if (i == MX0) {
-        mxa = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), fmaxf(s_nxt[0][2], s_nxt[0][3]));
-        mxb = fmaxf(fmaxf(s_nxt[0][4], s_nxt[0][5]), fmaxf(s_nxt[0][6], s_nxt[0][7]));
+        mxa = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), s_nxt[0][2]);
+        mxb = fmaxf(fmaxf(s_nxt[0][3], s_nxt[0][4]), s_nxt[0][5]);
 #pragma unroll
-        for (int r = 8; r < 16; r += 2) {
-          mxa = fmaxf(mxa, s_nxt[0][r]);
-          mxb = fmaxf(mxb, s_nxt[0][r + 1]);
+        for (int r = 6; r < 14; r += 4) {
+          mxa = fmaxf(fmaxf(mxa, s_nxt[0][r]), s_nxt[0][r + 1]);
+          mxb = fmaxf(fmaxf(mxb, s_nxt[0][r + 2]), s_nxt[0][r + 3]);
         }
+        mxa = fmaxf(fmaxf(mxa, s_nxt[0][14]), s_nxt[0][15]);
         pin(mxa);
         pin(mxb);
       }
       if (i == MX0 + 1) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          mxa = fmaxf(mxa, s_nxt[1][r]);
-          mxb = fmaxf(mxb, s_nxt[1][r + 1]);
+        for (int r = 0; r < 16; r += 4) {
+          mxa = fmaxf(fmaxf(mxa, s_nxt[1][r]), s_nxt[1][r + 1]);
+          mxb = fmaxf(fmaxf(mxb, s_nxt[1][r + 2]), s_nxt[1][r + 3]);
         }
         pin(mxa);
         pin(mxb);
       }
       if (i == MX0 + 2) {
-        float mx = fmaxf(mxa, mxb);
-        mx = fmaxf(mx, other_half(mx));
-        m_prev = m_cur;
-        offset_update(mx, m_cur, m_cur, a_cur);
-        pin(m_cur);
-        pin(a_cur);
+        const float mx = fmaxf(mxa, mxb);
+        mx_nxt = fmaxf(mx, other_half(mx));
+        pin(mx_nxt);
       }
     };
     v8 op[NM];
@@ -411,65 +484,56 @@ fwd16_kernel(FwdParams p) {
         acc[db] = M::mma(op[i], p_prev[t], acc[db]);
       }
       slice(i);
+      mem(i);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) p_cur[t] = __builtin_bit_cast(v8, pk[t]);
   };
 
-  // The per-tile step. Every pipeline block runs the same fused code; the
-  // edges are neutralised by data instead of separate code paths: a zero
-  // P_{j-1} (and a zeroed V buffer) makes PV a no-op, a fully masked S_j
-  // makes the softmax a no-op (P = 0), and an unneeded QK only computes a
-  // value that is never used. A wave skips the tiles past its causal range
-  // (j > wave_tiles) except for the memory work the whole workgroup shares.
-  // `par` is j mod 2, known at compile time (the loop is unrolled by two)
-  auto step = [&](int j, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+  // Step s (0 .. n_steps-1): one barrier, the offset decision for the wave's
+  // tile of step s and its block. Every block runs the same fused code; the
+  // edges are neutralised by data instead of separate code paths: a fully
+  // masked S_cur makes the softmax a no-op (P = 0, so the next block's P.V
+  // adds nothing), P_prev = 0 with a zeroed V buffer makes step 0's P.V a
+  // no-op, and an unneeded QK only computes a value that is never used.
+  // `par` is s mod 2, known at compile time (the loop is unrolled by two).
+  auto step = [&](int s, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
                   const v8(&p_prev)[4], v8(&p_cur)[4]) {
-    constexpr int J = decltype(par)::value;
-    constexpr int KS = (J + 1) % PD, VS = J % PD;  // register stages of K_{j+1}, V_j
-    // K_{j+1} into LDS (its global load was issued PD blocks ago); the loads
-    // and stores run unconditionally so that wait counts stay exact (a load
-    // past the keys reads zeros through the buffer bound)
-    lstore(kl[(j + 1) & 1], kreg[KS]);
+    // resources of the tiles this step's block loads: K(s+2+PD), V(s+PD)
+    const __amdgpu_buffer_rsrc_t rk[2] = {tile_rsrc(K, p.k_ss, 2 * (s + 2 + PD)),
+                                          tile_rsrc(K, p.k_ss, 2 * (s + 2 + PD) + 1)};
+    const __amdgpu_buffer_rsrc_t rv[2] = {tile_rsrc(V, p.v_ss, 2 * (s + PD)),
+                                          tile_rsrc(V, p.v_ss, 2 * (s + PD) + 1)};
     __syncthreads();
-    lstore(vl[j & 1], vreg[VS]);
-    gload(vreg[VS], V, p.v_ss, vroff, j + PD);
-    gload(kreg[KS], K, p.k_ss, kroff, j + 1 + PD);
-    if (j <= wave_tiles) {
-      const int kbase = j * BN;
-      if (j == wave_tiles) {
-        mask_all(s_cur);  // past this wave's range: a neutralised softmax
-        m_cur = m_prev;
-        a_cur = 1.f;
-      } else if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_len) {
+    bool rescale = false;
+    if (s >= wave_steps) {
+      mask_all(s_cur);
+      a_cur = 1.f;
+    } else {
+      const int kbase = (2 * s + g) * BN;  // this wave's current key tile
+      float mx = mx_nxt;
+      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_len) {
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf);
-        offset_update(row_max(s_cur), m_prev, m_cur, a_cur);  // redo with the mask
+        mx = row_max(s_cur);
       }
-      const bool rescale = __any(a_cur != 1.f);
-      const float a_blk = a_cur;
-      block(kl[(j + 1) & 1], vl[(j - 1) & 1], s_cur, s_nxt, p_prev, p_cur);
-      if (rescale) {
+      rescale = decide(mx);
+    }
+    const float a_blk = a_cur;
+    block(s, par, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+    if (rescale) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
-      }
+      for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
     }
   };
 
   if (n_tiles > 0) {
-    f32x16 sa[2], sb[2];
-    v8 pa[4], pb[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pa[t] = v8{};
-      pb[t] = v8{};
-    }
-    gload(kreg[0], K, p.k_ss, kroff, 0);
-#pragma unroll
-    for (int t = 0; t < PD; ++t) gload(vreg[t], V, p.v_ss, vroff, t);
-    // Q rows as B operands of S^T = K Q^T (lane holds Q[qi][16ks + 8hf .. +7]),
-    // loaded after the first K/V tiles are requested so that the two
-    // latencies overlap; rows past the sequence read as zeros
+    // Prologue: Q as B operands of S^T = K Q^T (lane holds
+    // Q[qi][16ks + 8hf .. +7]; rows past the sequence read as zeros); K(0)
+    // and K(1) into LDS, zeros into the V buffer that step 0's no-op P.V
+    // reads, and the register stages filled as step 0 expects them:
+    // K(2 .. 1+PD) and V(0 .. PD-1).
+    i16x8 qraw[D / 16];
     {
       const T* qb = Q + (int64_t)(qt * BM) * p.q_ss;
       const int rows = min(q_len - qt * BM, BM);
@@ -478,73 +542,145 @@ fwd16_kernel(FwdParams p) {
       const int qoff = (qi - qt * BM) * (int)p.q_ss * (int)sizeof(T) + 16 * hf;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        qraw[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, qoff + 32 * ks, 0, 0));
+        qraw[ks] = __builtin_bit_cast(
+            i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, qoff + 32 * ks, 0, 0));
     }
+    i16x8 k01[2][CPT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(K, p.k_ss, 2 * t),
+                                            tile_rsrc(K, p.k_ss, 2 * t + 1)};
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) k01[t][x] = kload(r2, x);
+    }
+#pragma unroll
+    for (int t = 2; t < 2 + PD; ++t) {
+      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(K, p.k_ss, 2 * t),
+                                            tile_rsrc(K, p.k_ss, 2 * t + 1)};
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) kreg[t % PD][x] = kload(r2, x);
+    }
+#pragma unroll
+    for (int t = 0; t < PD; ++t) {
+      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(V, p.v_ss, 2 * t),
+                                            tile_rsrc(V, p.v_ss, 2 * t + 1)};
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) vreg[t][x] = vload(r2, x);
+    }
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) *(i16x8*)&vl[1][0][vslot(x)] = i16x8{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       i16x8 raw = qraw[ks];
-      if (p.negate_q) raw ^= (short)0x8000;
+      if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
       qf[ks] = __builtin_bit_cast(v8, raw);
     }
-    lstore(kl[0], kreg[0]);
-    {
-      const i16x8 zero[CPT] = {};
-      lstore(vl[1], zero);  // read by the no-op P.V of the first block
-    }
 #pragma unroll
-    for (int t = 1; t <= PD; ++t) gload(kreg[t % PD], K, p.k_ss, kroff, t);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) *(i16x8*)&kl[t][0][kslot(x)] = k01[t][x];
+    f32x16 sa[2], sb[2];
+    v8 pa[4], pb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pa[t] = v8{};
+      pb[t] = v8{};
+    }
     __syncthreads();
-    // S_0 = QK(K_0) and its offset; the P.V and softmax parts are neutralised
-    // (sb fully masked, P_{-1} = 0, V buffer 1 zero)
-    mask_all(sb);
-    block(kl[0], vl[1], sb, sa, pb, pa);
-    int j = 0;
+    qk_only(kl[0][g], sa);  // S of step 0
+    // even steps: S_cur = sa, S_next = sb, P_prev = pb, P_cur = pa; odd
+    // steps the other way round
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    for (; j + 1 < n_tiles; j += 2) {
-      step(j, I0{}, sa, sb, pb, pa);
-      step(j + 1, I1{}, sb, sa, pa, pb);
+    int s = 0;
+    for (; s + 1 < n_steps; s += 2) {
+      step(s, I0{}, sa, sb, pb, pa);
+      step(s + 1, I1{}, sb, sa, pa, pb);
     }
-    if (j < n_tiles) {
-      step(j, I0{}, sa, sb, pb, pa);
-      ++j;
-    }
-    // drain: P.V of the last tile, whose V was stored in the last block; the
-    // block's softmax is neutralised (masked scores, factor 1 at the offset
-    // of l), and its new offset comes from unused scores and is discarded
+    if (s < n_steps) step(s, I0{}, sa, sb, pb, pa);
+    // the P.V of the wave's tile of the last step, if it had one
     __syncthreads();
-    if (j - 1 < wave_tiles) {
-      m_cur = m_l;
-      a_cur = 1.f;
-      if ((j - 1) & 1) {
-        mask_all(sa);
-        block(kl[0], vl[1], sa, sb, pb, pa);
-      } else {
-        mask_all(sb);
-        block(kl[0], vl[0], sb, sa, pa, pb);
-      }
+    if (wave_steps == n_steps) {
+      if ((n_steps - 1) & 1) pv_only(vl[1][g], pb);
+      else pv_only(vl[0][g], pa);
     }
   }
 
-  // Epilogue: combine the two halves' partial sums, normalise, store.
+  // Merge the two key groups of each row group through LDS and store. Wave
+  // w (group g) finalises d-half g of its 32 rows: it publishes the other
+  // half of its O^T with its (offset, l) in slot w, and merges its own half
+  // with the partner's (wave w ^ 4, the other group on the same SIMD). The
+  // K buffers hold the exchange (8 slots of NV floats per lane fill them
+  // exactly), the V buffers the per-wave transposes for the stores.
+  constexpr int NB = D / 64;      // accumulator blocks per d-half
+  constexpr int NV = 16 * NB + 2;  // floats per lane: half of O^T, offset, l
+  static_assert(8 * NV * 64 * 4 <= (int)sizeof(kl), "merge buffer too small");
+  float* xl = reinterpret_cast<float*>(&kl[0][0][0]);
+  // (the halves are selected with compile-time indices: a runtime index
+  // into acc would move the accumulator to scratch memory)
+  f32x16 mine[NB], other[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    mine[b] = g == 0 ? acc[b] : acc[NB + b];
+    other[b] = g == 0 ? acc[NB + b] : acc[b];
+  }
+  __syncthreads();  // every block has finished with the K/V buffers
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xl[(wave * NV + 16 * b + r) * 64 + lane] = other[b][r];
+  xl[(wave * NV + 16 * NB) * 64 + lane] = m_cur;
+  xl[(wave * NV + 16 * NB + 1) * 64 + lane] = l_run;
+  __syncthreads();
+  const int pw = wave ^ 4;
+  f32x16 oh[NB];  // this wave's d-half of O^T, merged
+  {
+    const float m1 = xl[(pw * NV + 16 * NB) * 64 + lane];
+    const float l1 = xl[(pw * NV + 16 * NB + 1) * 64 + lane];
+    const float m = fmaxf(m_cur, m1);
+    const float mr = m == -INFINITY ? 0.f : m;
+    const float f0 = fast_exp2(m_cur - mr), f1 = fast_exp2(m1 - mr);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oh[b][r] = mine[b][r] * f0 + xl[(pw * NV + 16 * b + r) * 64 + lane] * f1;
+    l_run = l_run * f0 + l1 * f1;
+    m_cur = m;
+  }
+
+  // Epilogue: combine the two lane halves' partial sums, normalise, and
+  // store through a per-wave LDS transpose so that each lane writes 16
+  // contiguous bytes and a store instruction covers whole row segments.
   const float l_tot = l_run + other_half(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_valid) {
-    T* orow = O + (int64_t)qi * p.o_ss;
+  constexpr int HD = D / 2;     // d values per half
+  constexpr int TP = HD + 8;    // transpose row pitch (elements)
+  static_assert(8 * 32 * TP * (int)sizeof(T) <= (int)sizeof(vl), "transpose buffer too small");
+  T* tl = &vl[0][0][0] + wave * 32 * TP;
+  typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        typedef T t4 __attribute__((ext_vector_type(4)));
-        t4 ov;
+    for (int rq = 0; rq < 4; ++rq) {
+      t4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
-        *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
-      }
-    if (hf == 0 && p.lse)
-      p.lse[lse_off + (int64_t)qi * lse_st] =
-          l_tot > 0.f ? (m_l + __log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) ov[e] = (T)(oh[b][4 * rq + e] * inv);
+      *(t4*)&tl[col * TP + 32 * b + 8 * rq + 4 * hf] = ov;
+    }
+  constexpr int CPR = HD / 8;           // 16-byte chunks per half row
+  constexpr int RPI = 64 / CPR;         // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, cc = lane % CPR;
+    const i16x8 v = *(const i16x8*)&tl[r * TP + 8 * cc];
+    if (row0 + r < q_len)
+      *(i16x8*)(O + (int64_t)(row0 + r) * p.o_ss + g * HD + 8 * cc) = v;
   }
+  if (g == 0 && hf == 0 && q_valid && p.lse)
+    p.lse[lse_off + (int64_t)qi * lse_st] =
+        l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }  // pass
 }
 
 // ---------------------------------------------------------------------------
@@ -679,8 +815,8 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 const void* pick_kernel(Dt dt) {
-  // fp16/bf16 kernels run 8-wave workgroups over pairs of query tiles;
-  // the fp32 kernel runs 4-wave workgroups over single query tiles.
+  // fp16/bf16 kernels run 8-wave split-key workgroups; the fp32 kernel runs
+  // 4-wave workgroups.
   switch (dt) {
     case Dt::BF16: return (const void*)&fwd16_kernel<__bf16, D, CAUSAL, VARLEN>;
     case Dt::F16: return (const void*)&fwd16_kernel<_Float16, D, CAUSAL, VARLEN>;
@@ -702,8 +838,10 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   const void* fn = d == 64 ? pick_kernel<64>(dt, causal, varlen)
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
+  // fp16/bf16: 8-wave split-key workgroups, over causal tile pairs
   const bool paired = dt != Dt::F32;
-  const long long grid = (long long)p.n_qtiles * p.b * p.h;
+  const long long grid =
+      (long long)(paired && causal ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};

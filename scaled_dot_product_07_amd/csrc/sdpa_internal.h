@@ -61,7 +61,7 @@ struct BwdParams {
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (32 per wave)
 constexpr int kFwdBlockN = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;    // fp32 forward workgroup
-constexpr int kFwdThreads16 = 256;  // fp16/bf16 forward workgroup
+constexpr int kFwdThreads16 = 512;  // fp16/bf16 forward workgroup (two key groups)
 
 // Enqueue the forward; returns the launch status.
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
