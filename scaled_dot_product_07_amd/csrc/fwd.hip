@@ -6,14 +6,19 @@
 // top-left causal band; cudnn-frontend PR #554: statistic layouts and THD
 // packing with cu_seqlens).
 //
-// One workgroup = 4 waves = 128 query rows of one (b, h) or (sequence, h).
-// Each wave owns 32 query rows and keeps, for the whole key loop:
-//   * its Q rows as MFMA B operands in VGPRs (loaded once),
+// fp16/bf16: one workgroup = 8 waves = one 128-row query tile of one
+// (b, h) or (sequence, h) (for causal attention: a pair of query tiles, one
+// after the other). Each wave owns 32 query rows and half of the key tiles
+// (waves w and w+4 split the keys of the same rows) and keeps, for the whole
+// key loop:
+//   * its Q rows as MFMA B operands in VGPRs,
 //   * the fp32 output accumulator O^T (d x 32) in the MFMA C layout,
-//   * the running max m and running sum l of its rows.
-// Keys are streamed in tiles of 64 rows of K and V through double-buffered
-// LDS: the global loads of tile j+1 are issued before tile j is computed and
-// written to the other buffer after it, with one barrier per tile.
+//   * the offset m and running sum l of its rows.
+// Keys are streamed in tiles of 64 rows of K and V, loaded by the buffer
+// loads' direct-to-LDS path into double-buffered LDS one step ahead of the
+// block that reads them, with one barrier per step (two tiles). The two
+// key-group partial results of a row are merged through LDS at the end.
+// fp32 io: 4 waves, 128 rows, one tile per step, loads through VGPRs.
 //
 // The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, on
 // v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2_f32 for fp32 io). In
@@ -33,15 +38,15 @@
 // Causal (top-left): query i sees key j iff j <= i. Key tiles past the last
 // visible key of the workgroup are never loaded; a wave skips the tiles past
 // its own last visible key, and only tiles that straddle the diagonal (or the
-// end of the keys) evaluate the mask. Loads of key rows at or beyond the
-// sequence's key count are predicated off and zero-filled, so padding or a
-// NaN-poisoned tail never reaches P.V (the FP8 d512 forward entry in the
-// cudnn-frontend PR #554 merge log describes that failure: masking zeroes P,
-// not V).
+// end of the keys) evaluate the mask. Key rows at or beyond the sequence's
+// key count read as zeros (a buffer bound, or a predicated load for fp32),
+// so padding or a NaN-poisoned tail never reaches P.V (the FP8 d512 forward
+// entry in the cudnn-frontend PR #554 merge log describes that failure:
+// masking zeroes P, not V).
 //
-// Work order: blockIdx -> (query tile, b*h) with the heaviest causal query
-// tiles first (longest-processing-time order), and all tiles of one (b, h)
-// on the same XCD when b*h is a multiple of 8, so they share its L2.
+// Work order: blockIdx -> (query tile or causal tile pair, b*h), so all
+// tiles of one (b, h) run on the same XCD when b*h is a multiple of 8 and
+// share its L2.
 
 #include <math.h>
 
@@ -52,6 +57,30 @@
 
 namespace sdpa07 {
 namespace {
+
+// Buffer resources (the four descriptor words) of the two key tiles of one
+// step.
+struct Rsrc2 {
+  i32x4 r[2];
+};
+
+// One 16-byte-per-lane buffer load into LDS: lane l's 16 bytes land at LDS
+// byte address lds_addr + 16 l. Written as inline assembly so that the
+// compiler does not treat later LDS reads as dependent on it (it would wait
+// for every such load before each transposing read); the kernels place the
+// vmcnt waits themselves. M0, which the instruction takes its LDS address
+// from, is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsigned lds_addr) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
 
 // Decoded work unit of one workgroup.
 struct Unit {
@@ -182,24 +211,33 @@ __global__ void __launch_bounds__(kFwdThreads16) __attribute__((amdgpu_waves_per
 fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int NT = kFwdThreads16;   // 8 waves
-  // Row pitches (elements). K: +16 B, so the 16 lanes of a ds_read_b128
-  // phase (16 rows) hit distinct banks. V: row stride = 64 B mod 256 B, so
-  // the four 64-byte row pieces that a transposing read covers per 32 lanes
-  // hit distinct banks.
-  constexpr int KP = D + 8;
-  constexpr int VP = D + 32;
-  constexpr int CH_ROW = D / 8;       // 16-byte chunks per row
-  constexpr int TILE_CH = BN * CH_ROW;
-  constexpr int CPT = 2 * TILE_CH / NT;  // chunks per thread per tensor per step (two tiles)
-  static_assert(CPT >= 1 && (2 * TILE_CH) % NT == 0, "tile/workgroup mismatch");
-  // chunk x of a thread lies in tile NT*x / TILE_CH for every thread, so each
-  // buffer resource is uniform over the wave
-  static_assert(TILE_CH % NT == 0, "a thread's chunk must not straddle tiles");
+  // K and V tiles go from memory straight into LDS (buffer loads with the
+  // LDS flag): a wave's load instruction fills 1 KB of LDS, lane l writing
+  // bytes [16l, 16l + 16). Rows are stored unpadded and each row's 16-byte
+  // chunks are permuted by an XOR swizzle of the row index, so that the QK^T
+  // operand reads (ds_read_b128, 16 rows per phase) and the transposing P.V
+  // operand reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes) hit
+  // distinct banks; each lane loads the global chunk that its slot holds.
+  // Tiles of step u live in buffer u mod NBK (K) / u mod NBV (V); a step's
+  // loads run LK (K) and LV (V) steps ahead of the block that reads them.
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;         // rows per load instruction
+  constexpr int CPT = 2 * BN / RPI / (NT / 64);  // load instructions per wave per tensor per step
+  static_assert(CPT >= 1 && (2 * BN) % (RPI * (NT / 64)) == 0, "tile/workgroup mismatch");
+  constexpr int NBK = 2, NBV = 2;
+  constexpr int LK = NBK - 1, LV = NBV - 1;
+  constexpr int TILE = BN * D;         // elements per tile
+  constexpr int KBUF = 2 * TILE, VBUF = 2 * TILE;  // one step: the two key groups' tiles
+  constexpr int LDS_ELEMS = NBK * KBUF + NBV * VBUF;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  // [buffer][key group][tile]
-  __shared__ __attribute__((aligned(16))) T kl[2][2][BN * KP];
-  __shared__ __attribute__((aligned(16))) T vl[2][2][BN * VP];
+  __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
+  T* const kbuf0 = lds;                 // [NBK][2][TILE]
+  T* const vbuf0 = lds + NBK * KBUF;    // [NBV][2][TILE]
+  // chunk permutation of row r (only r mod 16 matters)
+  auto swz = [](int r) -> int {
+    return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
+  };
 
   // ---- work unit: causal, a pair of query tiles (n-1-i, i) of one
   // (b|sequence, h), the heavier first, so that every pair holds the same
@@ -246,11 +284,32 @@ fwd16_kernel(FwdParams p) {
   const int rg = wave % 4;      // row group
   const int hf = lane / 32, col = lane % 32;
 
+  // s_waitcnt with only a vmcnt bound (gfx9 encoding: expcnt and lgkmcnt at
+  // their maxima)
+  auto wait_vm = [](auto n) {
+    constexpr int N = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  };
+  // Before the barrier of step s this wave's loads of K(s+1) and V(s-1) must
+  // have landed: they were issued in blocks s-LK and s-LV (V first, then K,
+  // in each block), so the loads allowed to be outstanding are those issued
+  // after the later of the two.
+  constexpr int WAITN = CPT * (2 * LK - 2 < 2 * LV - 1 ? 2 * LK - 2 : 2 * LV - 1);
+  using WaitStep = std::integral_constant<int, WAITN>;
+  // the prologue's loads issued after K(0): K(1 .. LK) and V(-1 .. LV-2)
+  using WaitK0 = std::integral_constant<int, CPT * (LK + LV)>;
+  using WaitAll = std::integral_constant<int, 0>;
+
   for (int pass = 0; pass < PASSES; ++pass) {
   const int qt = !CAUSAL ? pair : pass == 0 ? p.n_qtiles - 1 - pair : pair;
   if (pass == 1 && qt >= p.n_qtiles - 1 - pair) break;  // odd count: middle tile alone
   if (qt * BM >= q_len) continue;  // uniform over the workgroup
-  if (pass == 1) __syncthreads();  // the first tile's epilogue is done with LDS
+  if (pass == 1) {
+    // the first tile's epilogue is done with LDS, and its stores have left
+    // the counter that the load waits below count against
+    wait_vm(WaitAll{});
+    __syncthreads();
+  }
   const int row0 = qt * BM + rg * 32;  // first query row of this wave
   const int qi = row0 + col;           // this lane's query row
   const bool wave_active = row0 < q_len;
@@ -278,40 +337,45 @@ fwd16_kernel(FwdParams p) {
   // it read as zeros and are masked anyway (rows are disjoint when the row
   // stride is at least d, which every dense layout satisfies; with
   // overlapping rows the extra rows are real, finite keys that the mask
-  // hides), with no per-lane test and no memory touched past the keys.
-  // Chunk x of thread tid is row tid / CH_ROW + XROW(x) of tile XT(x), 16
-  // bytes at column (tid % CH_ROW) * 8; the per-x parts are uniform (a
-  // scalar offset of the buffer load) or constant (an LDS immediate).
-  auto XT = [](int x) { return NT * x / TILE_CH; };
-  auto XROW = [](int x) { return (NT * x % TILE_CH) / CH_ROW; };
-  const int kroff = (tid / CH_ROW) * (int)p.k_ss * (int)sizeof(T) + (tid % CH_ROW) * 16;
-  const int vroff = (tid / CH_ROW) * (int)p.v_ss * (int)sizeof(T) + (tid % CH_ROW) * 16;
-  const int kldso = (tid / CH_ROW) * KP + (tid % CH_ROW) * 8;
-  const int vldso = (tid / CH_ROW) * VP + (tid % CH_ROW) * 8;
+  // hides), with no per-lane test and no memory touched past the keys; a
+  // tile outside the keys is all zeros.
+  // Load instruction x of wave w covers rows RIT(x) .. RIT(x) + RPI - 1 of
+  // tile XT(x) of the step; lane l fills row RIT(x) + l / CH, slot l % CH.
+  // (the 8 waves' rows of one instruction x stay within one tile, so the
+  // tile is a compile-time function of x and the resource index is static)
+  static_assert((8 * RPI) % BN == 0 || BN % (8 * RPI) == 0, "instruction rows straddle tiles");
+  auto XT = [](int x) { return 8 * x * RPI / BN; };
+  auto RIT = [&](int x) { return 8 * x * RPI % BN + wave * RPI; };
+  const int drow = lane / CH;
+  const int dchunk = (lane % CH) ^ swz(RIT(0) % 16 + drow);  // RIT(x) mod 16 is the same for all x
+  const int kvoff = drow * (int)p.k_ss * (int)sizeof(T) + dchunk * 16;
+  const int vvoff = drow * (int)p.v_ss * (int)sizeof(T) + dchunk * 16;
   // buffer resource of key tile t (zero bytes for tiles outside the keys);
   // built in scalar code outside the fused blocks
-  auto tile_rsrc = [&](const T* __restrict__ base, int64_t stride,
-                       int t) -> __amdgpu_buffer_rsrc_t {
+  auto tile_rsrc = [&](const T* __restrict__ base, int64_t stride, int t) -> i32x4 {
     const T* tb = base + (int64_t)t * BN * stride;
     const int rows = t < 0 ? 0 : min(kv_end - t * BN, BN);
     const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, kBufferFlags);
+    const unsigned long long a = (unsigned long long)tb;
+    return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
   };
-  auto gload = [&](__amdgpu_buffer_rsrc_t rs, int voff, int soff) -> i16x8 {
-    return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+  auto dma = [&](i32x4 rs, int voff, int soff, T* dst) {
+    lds_dma16(rs, voff, soff,
+              (unsigned)(size_t)(__attribute__((address_space(3))) T*)dst);
   };
-  auto kload = [&](const __amdgpu_buffer_rsrc_t(&r2)[2], int x) -> i16x8 {
-    return gload(r2[XT(x)], kroff, XROW(x) * (int)p.k_ss * (int)sizeof(T));
+  // the loads of instruction x of step u's K (V) tiles into their buffer
+  // (u >= -1; step -1 is all zeros)
+  auto kdma = [&](const Rsrc2& r2, int u, int x) {
+    dma(r2.r[XT(x)], kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T),
+        kbuf0 + (u % NBK) * KBUF + XT(x) * TILE + RIT(x) * D);
   };
-  auto vload = [&](const __amdgpu_buffer_rsrc_t(&r2)[2], int x) -> i16x8 {
-    return gload(r2[XT(x)], vroff, XROW(x) * (int)p.v_ss * (int)sizeof(T));
+  auto vdma = [&](const Rsrc2& r2, int u, int x) {
+    dma(r2.r[XT(x)], vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T),
+        vbuf0 + ((u + NBV) % NBV) * VBUF + XT(x) * TILE + RIT(x) * D);
   };
-  auto kslot = [&](int x) { return XT(x) * BN * KP + XROW(x) * KP + kldso; };
-  auto vslot = [&](int x) { return XT(x) * BN * VP + XROW(x) * VP + vldso; };
-  // register stages between a tile's global load and its LDS store: the loads
-  // of K(s+2+PD) and V(s+PD) are issued in the block that stores K(s+2), V(s)
-  constexpr int PD = D <= 64 ? 2 : 1;
-  i16x8 kreg[PD][CPT], vreg[PD][CPT];
+  auto rsrc2 = [&](const T* __restrict__ base, int64_t stride, int u) -> Rsrc2 {
+    return Rsrc2{{tile_rsrc(base, stride, 2 * u), tile_rsrc(base, stride, 2 * u + 1)}};
+  };
 
   // Softmax state (per lane = per query row; both halves agree):
   //   m_cur  offset (log2 units) of the P that the next block computes; after
@@ -350,10 +414,10 @@ fwd16_kernel(FwdParams p) {
   //   SM  : P_cur = 2^(scores), row sum into l   (VALU, early chunks)
   //   MX  : row max of S_next                    (VALU, last chunks, once the
   //                                               QK results are complete)
-  //   MEM : this thread's LDS stores of K(s+2) and V(s) and global loads of
-  //         K(s+2+PD) and V(s+PD), one instruction per chunk
+  //   MEM : this wave's direct-to-LDS loads of V(s-1+LV) and K(s+1+LK),
+  //         one instruction per chunk
   // It is emitted as NM chunks, each = the LDS read for the MFMA PF chunks
-  // ahead, one MFMA, a slice of the VALU work and at most one memory op; the
+  // ahead, one MFMA, a slice of the VALU work and at most one load; the
   // slices are pinned to their chunk so the VALU work issues while the MFMA
   // pipe is busy.
   constexpr int NQK = 2 * (D / 16);
@@ -363,21 +427,27 @@ fwd16_kernel(FwdParams p) {
   constexpr int NPAIR = 16;                               // 32 scores per lane, in pairs
   constexpr int EXP_CHUNKS = NM - 6 < 16 ? NM - 6 : 16;   // chunks holding the exps
   constexpr int MX0 = NM - 4;                             // chunks MX0 .. MX0+2: max of S_next
-  constexpr int MEM0 = 1;                                 // chunks MEM0 .. MEM0+4*CPT-1
-  static_assert(MEM0 + 4 * CPT <= NM, "not enough chunks for the memory ops");
+  constexpr int MEM0 = 1;                                 // chunks MEM0 .. MEM0+2*CPT-1
+  static_assert(MEM0 + 2 * CPT <= NM, "not enough chunks for the memory ops");
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
   // MFMA A operands: K rows 32mb + col, d 16ks + 8hf .. +7 (S^T = K Q^T), and
-  // V^T rows (d) 32db + col for keys 16t + 8(e/4) + 4hf + e%4 (O^T = V^T P^T)
+  // V^T rows (d) 32db + col for keys 16t + 8(e/4) + 4hf + e%4 (O^T = V^T P^T).
+  // Element offsets within a tile carry the chunk swizzle (rows 32mb + col
+  // and 16t + r share the swizzle of col and r); they are loop-invariant
+  // (no per-lane arrays: an indexed private array could be moved to LDS).
+  const int sk = swz(col % 16), sv0 = swz(vrow), sv1 = swz(vrow + 8);
   auto read_k = [&](const T* kb, int ks, int mb) -> v8 {
-    return *(const v8*)&kb[(32 * mb + col) * KP + 16 * ks + 8 * hf];
+    return *(const v8*)&kb[(32 * mb + col) * D + (((2 * ks + hf) ^ sk) * 8)];
   };
   auto read_v = [&](const T* vb, int t, int db) -> v8 {
-    const T* a0 = vb + (16 * t + vrow) * VP + 32 * db + vcol;
+    const int c = 4 * db + vcol / 8;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(a0));
+        (__attribute__((address_space(3))) i16x4*)(vb + (16 * t + vrow) * D + ((c ^ sv0) * 8) +
+                                                   vcol % 8));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(a0 + 8 * VP));
+        (__attribute__((address_space(3))) i16x4*)(vb + (16 * t + vrow + 8) * D +
+                                                   ((c ^ sv1) * 8) + vcol % 8));
     return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // S of the first step alone (its P.V and softmax have nothing to do)
@@ -396,28 +466,19 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
   };
-  auto block = [&](int s, auto par, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
-                   const v8(&p_prev)[4], v8(&p_cur)[4], const __amdgpu_buffer_rsrc_t(&rk)[2],
-                   const __amdgpu_buffer_rsrc_t(&rv)[2]) {
-    constexpr int R = decltype(par)::value % PD;  // register stage of K(s+2) and V(s)
-    const T* kb = kl[(s + 1) & 1][g];  // K of step s+1
-    const T* vb = vl[(s + 1) & 1][g];  // V of step s-1
-    T* kw = kl[s & 1][0];              // K(s+2), both tiles
-    T* vw = vl[s & 1][0];              // V(s), both tiles
+  auto block = [&](int s, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
+                   v8(&p_cur)[4], const Rsrc2& rk, const Rsrc2& rv) {
+    const T* kb = kbuf0 + ((s + 1) % NBK) * KBUF + g * TILE;       // K of step s+1
+    const T* vb = vbuf0 + ((s + NBV - 1) % NBV) * VBUF + g * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
       if (i < NQK) return read_k(kb, i / 2, i % 2);
       return read_v(vb, (i - NQK) / (D / 32), (i - NQK) % (D / 32));
     };
-    auto mem = [&](int i) {
+    auto mem = [&](int i) {  // loads of V(s-1+LV), then K(s+1+LK)
       const int k = i - MEM0;
-      if (k < 0 || k >= 4 * CPT) return;
-      const int x = k % CPT;
-      switch (k / CPT) {
-        case 0: *(i16x8*)&kw[kslot(x)] = kreg[R][x]; break;
-        case 1: *(i16x8*)&vw[vslot(x)] = vreg[R][x]; break;
-        case 2: kreg[R][x] = kload(rk, x); break;
-        default: vreg[R][x] = vload(rv, x); break;
-      }
+      if (k < 0 || k >= 2 * CPT) return;
+      if (k < CPT) vdma(rv, s - 1 + LV, k);
+      else kdma(rk, s + 1 + LK, k - CPT);
     };
     const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
     float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
@@ -491,21 +552,21 @@ fwd16_kernel(FwdParams p) {
     for (int t = 0; t < 4; ++t) p_cur[t] = __builtin_bit_cast(v8, pk[t]);
   };
 
-  // Step s (0 .. n_steps-1): one barrier, the offset decision for the wave's
-  // tile of step s and its block. Every block runs the same fused code; the
-  // edges are neutralised by data instead of separate code paths: a fully
-  // masked S_cur makes the softmax a no-op (P = 0, so the next block's P.V
-  // adds nothing), P_prev = 0 with a zeroed V buffer makes step 0's P.V a
-  // no-op, and an unneeded QK only computes a value that is never used.
-  // `par` is s mod 2, known at compile time (the loop is unrolled by two).
-  auto step = [&](int s, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
-                  const v8(&p_prev)[4], v8(&p_cur)[4]) {
-    // resources of the tiles this step's block loads: K(s+2+PD), V(s+PD)
-    const __amdgpu_buffer_rsrc_t rk[2] = {tile_rsrc(K, p.k_ss, 2 * (s + 2 + PD)),
-                                          tile_rsrc(K, p.k_ss, 2 * (s + 2 + PD) + 1)};
-    const __amdgpu_buffer_rsrc_t rv[2] = {tile_rsrc(V, p.v_ss, 2 * (s + PD)),
-                                          tile_rsrc(V, p.v_ss, 2 * (s + PD) + 1)};
-    __syncthreads();
+  // Step s (0 .. n_steps-1): the wait for this wave's loads of the tiles the
+  // block reads, one barrier (every wave's loads have then landed, and every
+  // wave is done with the buffers this block's loads overwrite), the offset
+  // decision for the wave's tile of step s and its block. Every block runs
+  // the same fused code; the edges are neutralised by data instead of
+  // separate code paths: a fully masked S_cur makes the softmax a no-op
+  // (P = 0, so the next block's P.V adds nothing), P_prev = 0 with the zero
+  // tiles of step -1 makes step 0's P.V a no-op, and an unneeded QK only
+  // computes a value that is never used.
+  auto step = [&](int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
+                  v8(&p_cur)[4]) {
+    const Rsrc2 rk = rsrc2(K, p.k_ss, s + 1 + LK);
+    const Rsrc2 rv = rsrc2(V, p.v_ss, s - 1 + LV);
+    wait_vm(WaitStep{});
+    __builtin_amdgcn_s_barrier();
     bool rescale = false;
     if (s >= wave_steps) {
       mask_all(s_cur);
@@ -520,7 +581,7 @@ fwd16_kernel(FwdParams p) {
       rescale = decide(mx);
     }
     const float a_blk = a_cur;
-    block(s, par, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+    block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
     if (rescale) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
@@ -528,57 +589,43 @@ fwd16_kernel(FwdParams p) {
   };
 
   if (n_tiles > 0) {
-    // Prologue: Q as B operands of S^T = K Q^T (lane holds
-    // Q[qi][16ks + 8hf .. +7]; rows past the sequence read as zeros); K(0)
-    // and K(1) into LDS, zeros into the V buffer that step 0's no-op P.V
-    // reads, and the register stages filled as step 0 expects them:
-    // K(2 .. 1+PD) and V(0 .. PD-1).
-    i16x8 qraw[D / 16];
+    // Prologue: the query tile's 128 rows into LDS with the layout of one
+    // step's two K tiles (rows past the sequence read as zeros), in the V
+    // buffer that no load touches before block 0; then the loads that blocks
+    // -(LK+1) .. -1 would have issued, in the blocks' order (V(b-1+LV) when
+    // it is a step >= -1, then K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2)
+    // (V(-1), read by step 0's no-op P.V, is all zeros). Only Q and K(0)
+    // have to land before the first block; the steps' own waits cover the
+    // rest.
+    T* const qbuf = vbuf0 + (LV - 1) * VBUF;
     {
-      const T* qb = Q + (int64_t)(qt * BM) * p.q_ss;
-      const int rows = min(q_len - qt * BM, BM);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)qb, (short)0, ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T), kBufferFlags);
-      const int qoff = (qi - qt * BM) * (int)p.q_ss * (int)sizeof(T) + 16 * hf;
+      const int q_rows = q_len - qt * BM;
+      auto q_rsrc = [&](int h) -> i32x4 {
+        const T* qb = Q + (int64_t)(qt * BM + h * BN) * p.q_ss;
+        const int rows = min(q_rows - h * BN, BN);
+        const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T);
+        const unsigned long long a = (unsigned long long)qb;
+        return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
+      };
+      const Rsrc2 rq{{q_rsrc(0), q_rsrc(1)}};
+      const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + dchunk * 16;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        qraw[ks] = __builtin_bit_cast(
-            i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, qoff + 32 * ks, 0, 0));
-    }
-    i16x8 k01[2][CPT];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(K, p.k_ss, 2 * t),
-                                            tile_rsrc(K, p.k_ss, 2 * t + 1)};
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) k01[t][x] = kload(r2, x);
+      for (int x = 0; x < CPT; ++x)
+        dma(rq.r[XT(x)], qvoff, RIT(x) * (int)p.q_ss * (int)sizeof(T),
+            qbuf + XT(x) * TILE + RIT(x) * D);
     }
 #pragma unroll
-    for (int t = 2; t < 2 + PD; ++t) {
-      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(K, p.k_ss, 2 * t),
-                                            tile_rsrc(K, p.k_ss, 2 * t + 1)};
+    for (int b = -(LK + 1); b < 0; ++b) {
+      if (b - 1 + LV >= -1) {
+        const Rsrc2 r2 = rsrc2(V, p.v_ss, b - 1 + LV);
 #pragma unroll
-      for (int x = 0; x < CPT; ++x) kreg[t % PD][x] = kload(r2, x);
+        for (int x = 0; x < CPT; ++x) vdma(r2, b - 1 + LV, x);
+      }
+      const Rsrc2 r2 = rsrc2(K, p.k_ss, b + 1 + LK);
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) kdma(r2, b + 1 + LK, x);
     }
-#pragma unroll
-    for (int t = 0; t < PD; ++t) {
-      const __amdgpu_buffer_rsrc_t r2[2] = {tile_rsrc(V, p.v_ss, 2 * t),
-                                            tile_rsrc(V, p.v_ss, 2 * t + 1)};
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) vreg[t][x] = vload(r2, x);
-    }
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) *(i16x8*)&vl[1][0][vslot(x)] = i16x8{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      i16x8 raw = qraw[ks];
-      if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
-      qf[ks] = __builtin_bit_cast(v8, raw);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) *(i16x8*)&kl[t][0][kslot(x)] = k01[t][x];
+    static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
     f32x16 sa[2], sb[2];
     v8 pa[4], pb[4];
 #pragma unroll
@@ -586,23 +633,32 @@ fwd16_kernel(FwdParams p) {
       pa[t] = v8{};
       pb[t] = v8{};
     }
-    __syncthreads();
-    qk_only(kl[0][g], sa);  // S of step 0
+    wait_vm(WaitK0{});  // this wave's loads of Q and K(0); then every wave's
+    __builtin_amdgcn_s_barrier();
+    // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7]
+    // (read before the barrier of step 0, after which block 0 reloads qbuf)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      i16x8 raw = *(const i16x8*)&qbuf[(rg * 32 + col) * D + (((2 * ks + hf) ^ sk) * 8)];
+      if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
+      qf[ks] = __builtin_bit_cast(v8, raw);
+    }
+    qk_only(kbuf0 + g * TILE, sa);  // S of step 0 (K(0) is in buffer 0)
     // even steps: S_cur = sa, S_next = sb, P_prev = pb, P_cur = pa; odd
     // steps the other way round
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
     int s = 0;
     for (; s + 1 < n_steps; s += 2) {
-      step(s, I0{}, sa, sb, pb, pa);
-      step(s + 1, I1{}, sb, sa, pa, pb);
+      step(s, sa, sb, pb, pa);
+      step(s + 1, sb, sa, pa, pb);
     }
-    if (s < n_steps) step(s, I0{}, sa, sb, pb, pa);
+    if (s < n_steps) step(s, sa, sb, pb, pa);
     // the P.V of the wave's tile of the last step, if it had one
-    __syncthreads();
+    wait_vm(WaitStep{});
+    __builtin_amdgcn_s_barrier();
     if (wave_steps == n_steps) {
-      if ((n_steps - 1) & 1) pv_only(vl[1][g], pb);
-      else pv_only(vl[0][g], pa);
+      const T* vb = vbuf0 + ((n_steps - 1) % NBV) * VBUF + g * TILE;
+      if ((n_steps - 1) & 1) pv_only(vb, pb);
+      else pv_only(vb, pa);
     }
   }
 
@@ -614,8 +670,8 @@ fwd16_kernel(FwdParams p) {
   // exactly), the V buffers the per-wave transposes for the stores.
   constexpr int NB = D / 64;      // accumulator blocks per d-half
   constexpr int NV = 16 * NB + 2;  // floats per lane: half of O^T, offset, l
-  static_assert(8 * NV * 64 * 4 <= (int)sizeof(kl), "merge buffer too small");
-  float* xl = reinterpret_cast<float*>(&kl[0][0][0]);
+  static_assert(8 * NV * 64 * 4 <= (int)sizeof(lds), "merge buffer too small");
+  float* xl = reinterpret_cast<float*>(lds);
   // (the halves are selected with compile-time indices: a runtime index
   // into acc would move the accumulator to scratch memory)
   f32x16 mine[NB], other[NB];
@@ -624,7 +680,11 @@ fwd16_kernel(FwdParams p) {
     mine[b] = g == 0 ? acc[b] : acc[NB + b];
     other[b] = g == 0 ? acc[NB + b] : acc[b];
   }
-  __syncthreads();  // every block has finished with the K/V buffers
+  // every load of this wave has landed (the last blocks' loads past the keys
+  // still write zeros into their buffers), then every wave's; and every
+  // block has finished with the K/V buffers
+  wait_vm(WaitAll{});
+  __syncthreads();
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -656,8 +716,9 @@ fwd16_kernel(FwdParams p) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   constexpr int HD = D / 2;     // d values per half
   constexpr int TP = HD + 8;    // transpose row pitch (elements)
-  static_assert(8 * 32 * TP * (int)sizeof(T) <= (int)sizeof(vl), "transpose buffer too small");
-  T* tl = &vl[0][0][0] + wave * 32 * TP;
+  constexpr int XL_ELEMS = 8 * NV * 64 * 4 / (int)sizeof(T);  // the exchange area
+  static_assert(XL_ELEMS + 8 * 32 * TP <= LDS_ELEMS, "transpose buffer too small");
+  T* tl = lds + XL_ELEMS + wave * 32 * TP;
   typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int b = 0; b < NB; ++b)
