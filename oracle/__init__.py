@@ -52,12 +52,18 @@ def _load():
         I = ctypes.c_int
         lib.oracle_hardware_threads.restype = I
         lib.oracle_attn_rows.argtypes = [P, P, I64, P, P, I64, I64, D, I, P, P, I]
-        lib.oracle_fwd.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I, P, P, I]
-        lib.oracle_fwd_varlen.argtypes = [P, P, P, P, P, I64, I64, I64, D, I, P, P, I]
-        lib.oracle_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, I, P, P, P, P, P, I]
-        lib.oracle_bwd_varlen.argtypes = [P, P, P, P, P, P, I64, I64, I64, D, I, P, P, P, P, P, I]
-        for f in ("oracle_attn_rows", "oracle_fwd", "oracle_fwd_varlen", "oracle_bwd",
-                  "oracle_bwd_varlen"):
+        lib.oracle_attn_rows_ex.argtypes = [P, P, I64, I64, P, P, I64, I64, D, I, I, I64, P, P,
+                                            I]
+        lib.oracle_fwd_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, D, I, I, I64, P, P,
+                                      I]
+        lib.oracle_fwd_varlen_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, D, I, I, I64, P,
+                                             P, I]
+        lib.oracle_bwd_ex.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, D, I, I, I64, P,
+                                      P, P, P, P, I]
+        lib.oracle_bwd_varlen_ex.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, D, I, I, I64,
+                                             P, P, P, P, P, I]
+        for f in ("oracle_attn_rows", "oracle_attn_rows_ex", "oracle_fwd_ex",
+                  "oracle_fwd_varlen_ex", "oracle_bwd_ex", "oracle_bwd_varlen_ex"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -80,79 +86,102 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def fwd(q, k, v, scale: float, causal: bool, threads: int = 0):
-    """Dense forward. q [b,h,s_q,d], k/v [b,h,s_kv,d] -> (o [b,h,s_q,d], lse [b,h,s_q])."""
+def _mask(causal, bottom_right, window_left):
+    """Mask options as the oracle takes them (see oracle.cpp for their reading)."""
+    return int(bool(causal)), int(bool(bottom_right)), int(-1 if window_left is None else
+                                                          window_left)
+
+
+def fwd(q, k, v, scale: float, causal: bool, threads: int = 0, *, bottom_right: bool = False,
+        window_left: int = -1):
+    """Dense forward. q [b,h_q,s_q,d], k/v [b,h_kv,s_kv,d] (h_q a multiple of h_kv)
+    -> (o [b,h_q,s_q,d], lse [b,h_q,s_q])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     b, h, s_q, d = q.shape
-    s_kv = k.shape[2]
-    assert k.shape == (b, h, s_kv, d) and v.shape == (b, h, s_kv, d)
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    assert k.shape == (b, h_kv, s_kv, d) and v.shape == k.shape and h % h_kv == 0
     o = np.zeros((b, h, s_q, d))
     lse = np.zeros((b, h, s_q))
-    _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), b, h, s_q, s_kv, d, float(scale),
-                       int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    _load().oracle_fwd_ex(_ptr(q), _ptr(k), _ptr(v), b, h, h_kv, s_q, s_kv, d, float(scale),
+                          *_mask(causal, bottom_right, window_left), _ptr(o), _ptr(lse),
+                          int(threads))
     return o, lse
 
 
-def attn_rows(q_rows, q_pos, k, v, scale: float, causal: bool, threads: int = 0):
-    """Selected rows of one head. q_rows [n,d] at positions q_pos [n]; k/v [s_kv,d]."""
+def attn_rows(q_rows, q_pos, k, v, scale: float, causal: bool, threads: int = 0, *,
+              s_q: int = 0, bottom_right: bool = False, window_left: int = -1):
+    """Selected rows of one head. q_rows [n,d] at positions q_pos [n] of a problem with
+    s_q query rows (needed for bottom-right alignment); k/v [s_kv,d]."""
     q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     pos = np.ascontiguousarray(np.asarray(q_pos, dtype=np.int64))
     n, d = q_rows.shape
     s_kv = k.shape[0]
     assert pos.shape == (n,) and k.shape == (s_kv, d) and v.shape == (s_kv, d)
+    assert not bottom_right or s_q > 0
     o = np.zeros((n, d))
     lse = np.zeros((n,))
-    _load().oracle_attn_rows(_ptr(q_rows), _ptr(pos), n, _ptr(k), _ptr(v), s_kv, d,
-                             float(scale), int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    _load().oracle_attn_rows_ex(_ptr(q_rows), _ptr(pos), n, int(s_q), _ptr(k), _ptr(v), s_kv, d,
+                                float(scale), *_mask(causal, bottom_right, window_left), _ptr(o),
+                                _ptr(lse), int(threads))
     return o, lse
 
 
-def fwd_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0):
-    """Packed THD forward. q [T_q,h,d], k/v [T_kv,h,d], cu_* [n+1] -> (o [T_q,h,d], lse [T_q,h])."""
+def fwd_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0, *,
+               bottom_right: bool = False, window_left: int = -1):
+    """Packed THD forward. q [T_q,h_q,d], k/v [T_kv,h_kv,d], cu_* [n+1]
+    -> (o [T_q,h_q,d], lse [T_q,h_q])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu_q, cu_kv = _i32(cu_q), _i32(cu_kv)
     n = cu_q.shape[0] - 1
     t_q, h, d = q.shape
+    h_kv = k.shape[1]
     assert cu_kv.shape == cu_q.shape and cu_q[-1] <= t_q and cu_kv[-1] <= k.shape[0]
+    assert v.shape == k.shape and h % h_kv == 0
     o = np.zeros((t_q, h, d))
     lse = np.zeros((t_q, h))
-    _load().oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_kv), n, h, d,
-                              float(scale), int(bool(causal)), _ptr(o), _ptr(lse), int(threads))
+    _load().oracle_fwd_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_kv), n, h, h_kv,
+                                 d, float(scale), *_mask(causal, bottom_right, window_left),
+                                 _ptr(o), _ptr(lse), int(threads))
     return o, lse
 
 
-def bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0):
-    """Dense backward with the oracle's own forward.
+def bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0, *,
+        bottom_right: bool = False, window_left: int = -1):
+    """Dense backward with the oracle's own forward (heads as in fwd).
 
-    Returns (o, lse, dq, dk, dv), all float64, BHSD / [b,h,s_q].
+    Returns (o, lse, dq, dk, dv), all float64, BHSD / [b,h_q,s_q].
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     b, h, s_q, d = q.shape
-    s_kv = k.shape[2]
-    assert dout.shape == q.shape and k.shape == v.shape == (b, h, s_kv, d)
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    assert dout.shape == q.shape and k.shape == v.shape == (b, h_kv, s_kv, d) and h % h_kv == 0
     o = np.zeros_like(q)
     lse = np.zeros((b, h, s_q))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), b, h, s_q, s_kv, d, float(scale),
-                       int(bool(causal)), _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                       int(threads))
+    _load().oracle_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), b, h, h_kv, s_q, s_kv, d,
+                          float(scale), *_mask(causal, bottom_right, window_left), _ptr(o),
+                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
     return o, lse, dq, dk, dv
 
 
-def bwd_varlen(q, k, v, dout, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0):
+def bwd_varlen(q, k, v, dout, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0, *,
+               bottom_right: bool = False, window_left: int = -1):
     """Packed THD backward with the oracle's own forward. Returns (o, lse, dq, dk, dv)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     cu_q, cu_kv = _i32(cu_q), _i32(cu_kv)
     n = cu_q.shape[0] - 1
     t_q, h, d = q.shape
+    h_kv = k.shape[1]
+    assert v.shape == k.shape and h % h_kv == 0
     o = np.zeros_like(q)
     lse = np.zeros((t_q, h))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    _load().oracle_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_q), _ptr(cu_kv), n,
-                              h, d, float(scale), int(bool(causal)), _ptr(o), _ptr(lse), _ptr(dq),
-                              _ptr(dk), _ptr(dv), int(threads))
+    _load().oracle_bwd_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_q), _ptr(cu_kv),
+                                 n, h, h_kv, d, float(scale),
+                                 *_mask(causal, bottom_right, window_left), _ptr(o), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
     return o, lse, dq, dk, dv

@@ -32,9 +32,20 @@
 //    output comes from an all-zero P; a zero-length sequence contributes
 //    nothing.
 //
+//  * The same pull request's sdpa API: is_causal (top-left), causal_bottom_right
+//    (the diagonal aligned to the bottom-right corner, allowed only with an
+//    active band) and window_left (-1 = unbounded), and grouped-query
+//    attention (h_kv < h_q) served by the provider; its dense-backward tests
+//    note that GQA dK/dV sum over the h_q/h_kv query heads of a group.
+//
 // Readings taken where the pages are silent: causal is top-left even when
-// s_q != s_kv; a row with no visible key gets O = 0 and LSE = -inf; nothing is
-// rounded (the GPU's rounding of P and of outputs is absorbed by tolerances).
+// s_q != s_kv; bottom-right aligns query i with key i + s_kv - s_q (per
+// sequence in packed batches); window_left = W keeps the W keys left of the
+// aligned diagonal and the diagonal key itself (keys j >= p - W, inclusive),
+// and without causal only that left bound applies; query head hh reads K/V
+// head hh / (h_q / h_kv); a row with no visible key gets O = 0 and LSE =
+// -inf; nothing is rounded (the GPU's rounding of P and of outputs is
+// absorbed by tolerances).
 //
 // Layouts (all contiguous, row-major, double):
 //   dense : q, o [b][h][s_q][d]; k, v [b][h][s_kv][d]; lse [b][h][s_q]
@@ -70,20 +81,33 @@ void parallel_for(int64_t n, int threads, const std::function<void(int64_t)>& fn
   for (auto& th : pool) th.join();
 }
 
-// Key j is visible to the query at position i (cuDNN frontend demo, section
-// 5: causal = diagonal band aligned top-left with right bound 0).
-inline bool visible(int64_t i, int64_t j, int causal) { return !causal || j <= i; }
+// The mask options of one call (the sdpa API of cudnn-frontend PR #554).
+struct Mask {
+  int causal;        // right bound 0 on the aligned diagonal
+  int bottom_right;  // align the diagonal with the bottom-right corner
+  int64_t window;    // window_left; < 0: no left bound
+};
+
+// Key j is visible to the query at position i of a (s_q, s_kv) problem
+// (cuDNN frontend demo, section 5: causal = diagonal band with right bound 0,
+// aligned top-left; PR #554's sdpa: bottom-right alignment, window_left).
+inline bool visible(int64_t i, int64_t j, int64_t s_q, int64_t s_kv, const Mask& m) {
+  const int64_t p = m.bottom_right ? i + s_kv - s_q : i;  // diagonal key of row i
+  if (m.causal && j > p) return false;
+  if (m.window >= 0 && j < p - m.window) return false;
+  return true;
+}
 
 // One query row against one head's keys: the definition of softmax attention.
 // q: [d]; k, v: [s_kv][d] with row stride `kv_stride` elements; o: [d].
-void attend_row(const double* q, int64_t pos, const double* k, const double* v,
-                int64_t kv_stride, int64_t s_kv, int64_t d, double scale, int causal,
+void attend_row(const double* q, int64_t pos, int64_t s_q, const double* k, const double* v,
+                int64_t kv_stride, int64_t s_kv, int64_t d, double scale, const Mask& mask,
                 double* o, double* lse) {
   std::vector<double> x(s_kv > 0 ? s_kv : 1);
   double m = -std::numeric_limits<double>::infinity();
   int64_t n_vis = 0;
   for (int64_t j = 0; j < s_kv; ++j) {
-    if (!visible(pos, j, causal)) continue;
+    if (!visible(pos, j, s_q, s_kv, mask)) continue;
     double dot = 0.0;
     for (int64_t c = 0; c < d; ++c) dot += q[c] * k[j * kv_stride + c];
     x[j] = scale * dot;
@@ -97,22 +121,23 @@ void attend_row(const double* q, int64_t pos, const double* k, const double* v,
   }
   double l = 0.0;
   for (int64_t j = 0; j < s_kv; ++j)
-    if (visible(pos, j, causal)) l += std::exp(x[j] - m);
+    if (visible(pos, j, s_q, s_kv, mask)) l += std::exp(x[j] - m);
   const double L = m + std::log(l);
   *lse = L;
   for (int64_t j = 0; j < s_kv; ++j) {
-    if (!visible(pos, j, causal)) continue;
+    if (!visible(pos, j, s_q, s_kv, mask)) continue;
     const double p = std::exp(x[j] - L);
     for (int64_t c = 0; c < d; ++c) o[c] += p * v[j * kv_stride + c];
   }
 }
 
-// Backward of one head, given that head's forward O and LSE (fp64).
+// Backward of one query head, given that head's forward O and LSE (fp64).
 // Row strides let the same routine serve dense (stride d) and packed THD
-// (stride h*d) heads.
+// (stride h*d) heads. dQ is written; dK and dV are ADDED to (a K/V head
+// collects the contributions of every query head of its group).
 void backward_head(const double* q, const double* k, const double* v, const double* o,
                    const double* dout, const double* lse, int64_t qs, int64_t ks,
-                   int64_t s_q, int64_t s_kv, int64_t d, double scale, int causal,
+                   int64_t s_q, int64_t s_kv, int64_t d, double scale, const Mask& mask,
                    double* dq, double* dk, double* dv, int threads) {
   // P and dS as full [s_q][s_kv] matrices (zero where the key is hidden).
   std::vector<double> P((size_t)(s_q * s_kv)), dS((size_t)(s_q * s_kv));
@@ -124,7 +149,7 @@ void backward_head(const double* q, const double* k, const double* v, const doub
     for (int64_t c = 0; c < d; ++c) D += gi[c] * oi[c];
     for (int64_t j = 0; j < s_kv; ++j) {
       double p = 0.0, ds = 0.0;
-      if (visible(i, j, causal) && std::isfinite(lse[i])) {
+      if (visible(i, j, s_q, s_kv, mask) && std::isfinite(lse[i])) {
         double dot = 0.0, dp = 0.0;
         for (int64_t c = 0; c < d; ++c) {
           dot += qi[c] * k[j * ks + c];
@@ -153,8 +178,8 @@ void backward_head(const double* q, const double* k, const double* v, const doub
         ak += dS[(size_t)(i * s_kv + j)] * q[i * qs + c];
         av += P[(size_t)(i * s_kv + j)] * dout[i * qs + c];
       }
-      dk[j * ks + c] = scale * ak;
-      dv[j * ks + c] = av;
+      dk[j * ks + c] += scale * ak;
+      dv[j * ks + c] += av;
     }
   });
 }
@@ -167,81 +192,138 @@ int oracle_hardware_threads(void) {
   return (int)std::max(1u, std::thread::hardware_concurrency());
 }
 
-// Selected query rows of one head: row r of q sits at position q_pos[r]
-// (used for the causal test) and attends to all s_kv rows of k, v.
+// Selected query rows of one head: row r of q sits at position q_pos[r] of a
+// problem with s_q query rows and attends to the s_kv rows of k, v.
 // q, o: [n_q][d]; k, v: [s_kv][d]; lse: [n_q].
-void oracle_attn_rows(const double* q, const int64_t* q_pos, int64_t n_q, const double* k,
-                      const double* v, int64_t s_kv, int64_t d, double scale, int causal,
-                      double* o, double* lse, int threads) {
+void oracle_attn_rows_ex(const double* q, const int64_t* q_pos, int64_t n_q, int64_t s_q,
+                         const double* k, const double* v, int64_t s_kv, int64_t d, double scale,
+                         int causal, int bottom_right, int64_t window, double* o, double* lse,
+                         int threads) {
+  const Mask mask{causal, bottom_right, window};
   parallel_for(n_q, threads, [&](int64_t r) {
-    attend_row(q + r * d, q_pos[r], k, v, d, s_kv, d, scale, causal, o + r * d, lse + r);
+    attend_row(q + r * d, q_pos[r], s_q, k, v, d, s_kv, d, scale, mask, o + r * d, lse + r);
   });
 }
 
-// Dense forward, BHSD contiguous.
+void oracle_attn_rows(const double* q, const int64_t* q_pos, int64_t n_q, const double* k,
+                      const double* v, int64_t s_kv, int64_t d, double scale, int causal,
+                      double* o, double* lse, int threads) {
+  oracle_attn_rows_ex(q, q_pos, n_q, 0, k, v, s_kv, d, scale, causal, 0, -1, o, lse, threads);
+}
+
+// Dense forward, BHSD contiguous; q, o have h_q heads, k, v have h_kv heads
+// (h_q a multiple of h_kv).
+void oracle_fwd_ex(const double* q, const double* k, const double* v, int64_t b, int64_t h_q,
+                   int64_t h_kv, int64_t s_q, int64_t s_kv, int64_t d, double scale, int causal,
+                   int bottom_right, int64_t window, double* o, double* lse, int threads) {
+  const Mask mask{causal, bottom_right, window};
+  const int64_t group = h_q / h_kv;
+  parallel_for(b * h_q * s_q, threads, [&](int64_t r) {
+    const int64_t bh = r / s_q, i = r % s_q;
+    const int64_t bi = bh / h_q, hq = bh % h_q;
+    const int64_t kvo = (bi * h_kv + hq / group) * s_kv * d;
+    attend_row(q + r * d, i, s_q, k + kvo, v + kvo, d, s_kv, d, scale, mask, o + r * d, lse + r);
+  });
+}
+
 void oracle_fwd(const double* q, const double* k, const double* v, int64_t b, int64_t h,
                 int64_t s_q, int64_t s_kv, int64_t d, double scale, int causal, double* o,
                 double* lse, int threads) {
-  parallel_for(b * h * s_q, threads, [&](int64_t r) {
-    const int64_t bh = r / s_q, i = r % s_q;
-    attend_row(q + r * d, i, k + bh * s_kv * d, v + bh * s_kv * d, d, s_kv, d, scale, causal,
-               o + r * d, lse + r);
-  });
+  oracle_fwd_ex(q, k, v, b, h, h, s_q, s_kv, d, scale, causal, 0, -1, o, lse, threads);
 }
 
 // Packed THD forward. Sequence n owns tokens [cu_q[n], cu_q[n+1]) of q and
 // [cu_kv[n], cu_kv[n+1]) of k, v; positions are local to the sequence.
-void oracle_fwd_varlen(const double* q, const double* k, const double* v, const int32_t* cu_q,
-                       const int32_t* cu_kv, int64_t n_seqs, int64_t h, int64_t d, double scale,
-                       int causal, double* o, double* lse, int threads) {
+// q, o: [T_q][h_q][d]; k, v: [T_kv][h_kv][d]; lse: [T_q][h_q].
+void oracle_fwd_varlen_ex(const double* q, const double* k, const double* v, const int32_t* cu_q,
+                          const int32_t* cu_kv, int64_t n_seqs, int64_t h_q, int64_t h_kv,
+                          int64_t d, double scale, int causal, int bottom_right, int64_t window,
+                          double* o, double* lse, int threads) {
+  const Mask mask{causal, bottom_right, window};
+  const int64_t group = h_q / h_kv;
   const int64_t total_q = n_seqs > 0 ? cu_q[n_seqs] : 0;
-  parallel_for(total_q * h, threads, [&](int64_t r) {
-    const int64_t t = r / h, hh = r % h;
+  parallel_for(total_q * h_q, threads, [&](int64_t r) {
+    const int64_t t = r / h_q, hh = r % h_q;
     int64_t n = 0;
     while (n + 1 < n_seqs && cu_q[n + 1] <= t) ++n;  // sequence owning token t
-    const int64_t pos = t - cu_q[n];
+    const int64_t pos = t - cu_q[n], s_q = cu_q[n + 1] - cu_q[n];
     const int64_t kv0 = cu_kv[n], s_kv = cu_kv[n + 1] - cu_kv[n];
-    attend_row(q + (t * h + hh) * d, pos, k + (kv0 * h + hh) * d, v + (kv0 * h + hh) * d, h * d,
-               s_kv, d, scale, causal, o + (t * h + hh) * d, lse + t * h + hh);
+    const int64_t kvo = (kv0 * h_kv + hh / group) * d;
+    attend_row(q + (t * h_q + hh) * d, pos, s_q, k + kvo, v + kvo, h_kv * d, s_kv, d, scale,
+               mask, o + (t * h_q + hh) * d, lse + t * h_q + hh);
   });
 }
 
-// Dense backward, BHSD contiguous. Runs its own fp64 forward for O and LSE
-// (returned in o and lse), then the backward of every head.
+void oracle_fwd_varlen(const double* q, const double* k, const double* v, const int32_t* cu_q,
+                       const int32_t* cu_kv, int64_t n_seqs, int64_t h, int64_t d, double scale,
+                       int causal, double* o, double* lse, int threads) {
+  oracle_fwd_varlen_ex(q, k, v, cu_q, cu_kv, n_seqs, h, h, d, scale, causal, 0, -1, o, lse,
+                       threads);
+}
+
+// Dense backward, BHSD contiguous (heads as in oracle_fwd_ex). Runs its own
+// fp64 forward for O and LSE (returned in o and lse), then the backward of
+// every query head; a K/V head's dK and dV sum over its group.
+void oracle_bwd_ex(const double* q, const double* k, const double* v, const double* dout,
+                   int64_t b, int64_t h_q, int64_t h_kv, int64_t s_q, int64_t s_kv, int64_t d,
+                   double scale, int causal, int bottom_right, int64_t window, double* o,
+                   double* lse, double* dq, double* dk, double* dv, int threads) {
+  const Mask mask{causal, bottom_right, window};
+  const int64_t group = h_q / h_kv;
+  oracle_fwd_ex(q, k, v, b, h_q, h_kv, s_q, s_kv, d, scale, causal, bottom_right, window, o, lse,
+                threads);
+  std::memset(dk, 0, sizeof(double) * (size_t)(b * h_kv * s_kv * d));
+  std::memset(dv, 0, sizeof(double) * (size_t)(b * h_kv * s_kv * d));
+  for (int64_t bh = 0; bh < b * h_q; ++bh) {
+    const int64_t bi = bh / h_q, hq = bh % h_q;
+    const int64_t qo = bh * s_q * d, ko = (bi * h_kv + hq / group) * s_kv * d;
+    backward_head(q + qo, k + ko, v + ko, o + qo, dout + qo, lse + bh * s_q, d, d, s_q, s_kv, d,
+                  scale, mask, dq + qo, dk + ko, dv + ko, threads);
+  }
+}
+
 void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
                 int64_t b, int64_t h, int64_t s_q, int64_t s_kv, int64_t d, double scale,
                 int causal, double* o, double* lse, double* dq, double* dk, double* dv,
                 int threads) {
-  oracle_fwd(q, k, v, b, h, s_q, s_kv, d, scale, causal, o, lse, threads);
-  for (int64_t bh = 0; bh < b * h; ++bh) {
-    const int64_t qo = bh * s_q * d, ko = bh * s_kv * d;
-    backward_head(q + qo, k + ko, v + ko, o + qo, dout + qo, lse + bh * s_q, d, d, s_q, s_kv, d,
-                  scale, causal, dq + qo, dk + ko, dv + ko, threads);
-  }
+  oracle_bwd_ex(q, k, v, dout, b, h, h, s_q, s_kv, d, scale, causal, 0, -1, o, lse, dq, dk, dv,
+                threads);
 }
 
-// Packed THD backward, same conventions as oracle_fwd_varlen.
-void oracle_bwd_varlen(const double* q, const double* k, const double* v, const double* dout,
-                       const int32_t* cu_q, const int32_t* cu_kv, int64_t n_seqs, int64_t h,
-                       int64_t d, double scale, int causal, double* o, double* lse, double* dq,
-                       double* dk, double* dv, int threads) {
-  oracle_fwd_varlen(q, k, v, cu_q, cu_kv, n_seqs, h, d, scale, causal, o, lse, threads);
+// Packed THD backward, same conventions as oracle_fwd_varlen_ex.
+void oracle_bwd_varlen_ex(const double* q, const double* k, const double* v, const double* dout,
+                          const int32_t* cu_q, const int32_t* cu_kv, int64_t n_seqs, int64_t h_q,
+                          int64_t h_kv, int64_t d, double scale, int causal, int bottom_right,
+                          int64_t window, double* o, double* lse, double* dq, double* dk,
+                          double* dv, int threads) {
+  const Mask mask{causal, bottom_right, window};
+  const int64_t group = h_q / h_kv;
+  oracle_fwd_varlen_ex(q, k, v, cu_q, cu_kv, n_seqs, h_q, h_kv, d, scale, causal, bottom_right,
+                       window, o, lse, threads);
   const int64_t total_kv = n_seqs > 0 ? cu_kv[n_seqs] : 0;
-  std::memset(dk, 0, sizeof(double) * (size_t)(total_kv * h * d));
-  std::memset(dv, 0, sizeof(double) * (size_t)(total_kv * h * d));
+  std::memset(dk, 0, sizeof(double) * (size_t)(total_kv * h_kv * d));
+  std::memset(dv, 0, sizeof(double) * (size_t)(total_kv * h_kv * d));
   for (int64_t n = 0; n < n_seqs; ++n) {
     const int64_t q0 = cu_q[n], sq = cu_q[n + 1] - cu_q[n];
     const int64_t k0 = cu_kv[n], skv = cu_kv[n + 1] - cu_kv[n];
     if (sq == 0 && skv == 0) continue;
-    // lse is [t][h]: gather one head's column for this sequence.
-    for (int64_t hh = 0; hh < h; ++hh) {
+    // lse is [t][h_q]: gather one head's column for this sequence.
+    for (int64_t hh = 0; hh < h_q; ++hh) {
       std::vector<double> lse_h((size_t)std::max<int64_t>(sq, 1));
-      for (int64_t i = 0; i < sq; ++i) lse_h[(size_t)i] = lse[(q0 + i) * h + hh];
-      const int64_t qo = (q0 * h + hh) * d, ko = (k0 * h + hh) * d;
-      backward_head(q + qo, k + ko, v + ko, o + qo, dout + qo, lse_h.data(), h * d, h * d, sq,
-                    skv, d, scale, causal, dq + qo, dk + ko, dv + ko, threads);
+      for (int64_t i = 0; i < sq; ++i) lse_h[(size_t)i] = lse[(q0 + i) * h_q + hh];
+      const int64_t qo = (q0 * h_q + hh) * d, ko = (k0 * h_kv + hh / group) * d;
+      backward_head(q + qo, k + ko, v + ko, o + qo, dout + qo, lse_h.data(), h_q * d, h_kv * d,
+                    sq, skv, d, scale, mask, dq + qo, dk + ko, dv + ko, threads);
     }
   }
+}
+
+void oracle_bwd_varlen(const double* q, const double* k, const double* v, const double* dout,
+                       const int32_t* cu_q, const int32_t* cu_kv, int64_t n_seqs, int64_t h,
+                       int64_t d, double scale, int causal, double* o, double* lse, double* dq,
+                       double* dk, double* dv, int threads) {
+  oracle_bwd_varlen_ex(q, k, v, dout, cu_q, cu_kv, n_seqs, h, h, d, scale, causal, 0, -1, o, lse,
+                       dq, dk, dv, threads);
 }
 
 }  // extern "C"
