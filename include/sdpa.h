@@ -103,6 +103,45 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int causal, void* stream);
 
 /*
+ * Dense forward with grouped-query heads and the band options.
+ *   As sdpa_fwd, with:
+ *   h, h_kv: query heads and key/value heads; h must be a positive multiple
+ *     of h_kv, and query head i reads K/V head i / (h / h_kv) (h_kv == h is
+ *     plain multi-head attention, h_kv == 1 multi-query); k, v are
+ *     (b, h_kv, s_kv, d).
+ *   causal: 0 or 1: keys right of the aligned diagonal are hidden.
+ *   bottom_right: 0 aligns the diagonal top-left (query i with key i), 1
+ *     bottom-right (query i with key i + s_kv - s_q); 1 needs causal or a
+ *     window (SDPA_ERR_INVALID_ARG otherwise).
+ *   window_left: -1 for none, else W >= 0: keys more than W left of the
+ *     aligned diagonal are hidden (query i keeps keys p - W .. p, and with
+ *     causal = 0 every key from p - W on, where p is its diagonal key).
+ *   Rows left with no visible key get O = 0 and LSE = -inf.
+ * Cited: cudnn-frontend PR #554, the sdpa API (is_causal, causal_bottom_right,
+ * window_left; bottom-right without an active band is rejected) and the
+ * provider's GQA support; the cuDNN Graph API article, section 5 (the
+ * causal mask as a diagonal band with right bound 0).
+ */
+sdpa_status sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        sdpa_dtype dtype, int b, int h, int h_kv, int s_q, int s_kv, int d,
+                        const int64_t q_stride[4], const int64_t k_stride[4],
+                        const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                        int causal, int bottom_right, int window_left, void* stream);
+
+/*
+ * Packed THD forward with grouped-query heads and the band options (as
+ * sdpa_fwd_varlen and sdpa_fwd_ex): k, v are (total_kv, h_kv, d); the
+ * bottom-right alignment uses each sequence's own lengths.
+ */
+sdpa_status sdpa_fwd_varlen_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                               int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                               int max_seqlen_kv, sdpa_dtype dtype, int h, int h_kv, int d,
+                               const int64_t q_stride[3], const int64_t k_stride[3],
+                               const int64_t v_stride[3], const int64_t o_stride[3], float scale,
+                               int causal, int bottom_right, int window_left, void* stream);
+
+/*
  * Bytes of device workspace sdpa_bwd needs for these sizes: two fp32 values
  * per query row (rowsum(dO * O) and the statistic in base 2), rounded up to
  * 256 bytes. The caller allocates it (256-byte aligned).

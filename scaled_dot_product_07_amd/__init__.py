@@ -9,10 +9,13 @@ and passes pointers, strides and the current HIP stream across the ABI.
 If the library has not been built, importing works but every call raises
 ``RuntimeError``: there is no fallback path.
 
-Entry points (same names as the C ABI, minus the ``sdpa_`` prefix):
+Entry points (same names as the C ABI, minus the ``sdpa_`` prefix; the
+``_ex`` variants of the ABI are reached through the keyword options):
   fwd(q, k, v, ...)                       dense forward, returns (o, lse)
   fwd_varlen(q, k, v, cu_q, cu_kv, ...)   packed THD forward, returns (o, lse)
   bwd(q, k, v, o, dout, lse, ...)         dense backward, returns (dq, dk, dv)
+Options: grouped-query heads (k, v with fewer heads than q), causal,
+bottom_right (diagonal aligned to the bottom-right corner), window_left.
 """
 
 from __future__ import annotations
@@ -57,13 +60,17 @@ def _load():
     S4 = ctypes.c_int64 * 4
     S3 = ctypes.c_int64 * 3
     lib.sdpa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S4, S4, S4, S4, F, I, P]
+    lib.sdpa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, S4, S4, S4, S4, F, I, I, I,
+                                P]
     lib.sdpa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                     S3, S3, S3, S3, F, I, P]
+    lib.sdpa_fwd_varlen_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                       S3, S3, S3, S3, F, I, I, I, P]
     lib.sdpa_bwd_workspace_size.argtypes = [I, I, I, I, I]
     lib.sdpa_bwd_workspace_size.restype = Z
     lib.sdpa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I,
                              S4, S4, S4, S4, S4, S4, S4, S4, F, I, P]
-    for f in ("sdpa_fwd", "sdpa_fwd_varlen", "sdpa_bwd"):
+    for f in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd"):
         getattr(lib, f).restype = I
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.restype = ctypes.c_char_p
@@ -118,20 +125,22 @@ def _same_dtype(*ts):
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
-        causal: bool = False, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        causal: bool = False, bottom_right: bool = False, window_left: int = -1,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        return_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Dense forward on logical (b, h, s, d) tensors of any strides (d stride 1).
 
-    Returns (o, lse): o like q (same strides when q is dense), lse fp32 (b, h, s_q).
-    scale defaults to 1/sqrt(d); causal is top-left.
+    k, v may have fewer heads than q (grouped-query attention; h a multiple of
+    h_kv). Returns (o, lse): o like q (same strides when q is dense), lse fp32
+    (b, h, s_q). scale defaults to 1/sqrt(d); causal is top-left unless
+    bottom_right; window_left -1 means no left bound.
     """
     lib = _load()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("dense path expects 4-D (b, h, s, d) tensors")
     b, h, s_q, d = q.shape
-    s_kv = k.shape[2]
-    if tuple(k.shape) != (b, h, s_kv, d) or tuple(v.shape) != (b, h, s_kv, d):
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     _same_dtype(q, k, v, out)
     if out is None:
@@ -142,9 +151,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
                             or tuple(lse.shape) != (b, h, s_q)):
         raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    st = lib.sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
-                      b, h, s_q, s_kv, d, _strides(q, 4), _strides(k, 4), _strides(v, 4),
-                      _strides(out, 4), scale, int(bool(causal)), _stream(stream))
+    st = lib.sdpa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                         b, h, h_kv, s_q, s_kv, d, _strides(q, 4), _strides(k, 4),
+                         _strides(v, 4), _strides(out, 4), scale, int(bool(causal)),
+                         int(bool(bottom_right)), int(window_left), _stream(stream))
     _check(st)
     return out, lse
 
@@ -152,10 +162,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int, *,
                total_q: Optional[int] = None, total_kv: Optional[int] = None,
-               scale: Optional[float] = None, causal: bool = False,
-               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               return_lse: bool = True, stream=None):
-    """Packed THD forward: q (T_q, h, d), k/v (T_kv, h, d), int32 cu_seqlens on the device.
+               scale: Optional[float] = None, causal: bool = False, bottom_right: bool = False,
+               window_left: int = -1, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Packed THD forward: q (T_q, h, d), k/v (T_kv, h_kv, d), int32 cu_seqlens on the device.
 
     total_q / total_kv default to the tensors' first dims (rows beyond them are
     never touched). Returns (o, lse) with lse fp32 (T_q, h) token-major.
@@ -170,8 +180,8 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     if not (cu_seqlens_q.is_contiguous() and cu_seqlens_kv.is_contiguous()):
         raise ValueError("cu_seqlens must be contiguous")
     t_q, h, d = q.shape
-    t_kv = k.shape[0]
-    if tuple(k.shape[1:]) != (h, d) or tuple(v.shape) != tuple(k.shape):
+    t_kv, h_kv = k.shape[0], k.shape[1]
+    if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch between q, k, v")
     _same_dtype(q, k, v, out)
     total_q = t_q if total_q is None else int(total_q)
@@ -187,11 +197,12 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
                             or lse.shape[1:] != (h,) or lse.shape[0] < total_q):
         raise ValueError("lse must be a contiguous float32 (T_q, h) tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    st = lib.sdpa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                             _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), n, total_q, total_kv,
-                             int(max_seqlen_q), int(max_seqlen_kv), _dtype_code(q), h, d,
-                             _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(out, 3),
-                             scale, int(bool(causal)), _stream(stream))
+    st = lib.sdpa_fwd_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), n, total_q, total_kv,
+                                int(max_seqlen_q), int(max_seqlen_kv), _dtype_code(q), h, h_kv,
+                                d, _strides(q, 3), _strides(k, 3), _strides(v, 3),
+                                _strides(out, 3), scale, int(bool(causal)),
+                                int(bool(bottom_right)), int(window_left), _stream(stream))
     _check(st)
     return out, lse
 

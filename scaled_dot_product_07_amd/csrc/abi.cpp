@@ -106,6 +106,28 @@ sdpa_status launch_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Mask options (cudnn-frontend PR #554's sdpa API: is_causal,
+// causal_bottom_right, window_left; bottom-right alignment needs a band).
+sdpa_status check_mask(int causal, int bottom_right, int window_left) {
+  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (bottom_right != 0 && bottom_right != 1)
+    return fail(SDPA_ERR_INVALID_ARG, "bottom_right must be 0 or 1");
+  if (window_left < -1)
+    return fail(SDPA_ERR_INVALID_ARG, "window_left %d (expected >= 0, or -1 for none)",
+                window_left);
+  if (bottom_right && !causal && window_left < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "bottom_right needs causal or a window_left >= 0");
+  return SDPA_OK;
+}
+
+// Query heads h read K/V head i / (h / h_kv): h a positive multiple of h_kv.
+sdpa_status check_heads(int h, int h_kv) {
+  if (h_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "negative h_kv %d", h_kv);
+  if (h > 0 && (h_kv == 0 || h % h_kv != 0))
+    return fail(SDPA_ERR_INVALID_ARG, "h_q %d is not a multiple of h_kv %d", h, h_kv);
+  return SDPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,21 +136,22 @@ const char* sdpa_last_error(void) { return g_last_error.c_str(); }
 
 const char* sdpa_version(void) { return "sdpa07 0.1.0 gfx950"; }
 
-sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                     sdpa_dtype dtype, int b, int h, int s_q, int s_kv, int d,
-                     const int64_t q_stride[4], const int64_t k_stride[4],
-                     const int64_t v_stride[4], const int64_t o_stride[4], float scale,
-                     int causal, void* stream) {
+sdpa_status sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        sdpa_dtype dtype, int b, int h, int h_kv, int s_q, int s_kv, int d,
+                        const int64_t q_stride[4], const int64_t k_stride[4],
+                        const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                        int causal, int bottom_right, int window_left, void* stream) {
   if (!valid_dtype(dtype)) return fail(SDPA_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
   if (b < 0 || h < 0 || s_q < 0 || s_kv < 0 || d < 0)
     return fail(SDPA_ERR_INVALID_ARG, "negative size (b=%d h=%d s_q=%d s_kv=%d d=%d)", b, h, s_q,
                 s_kv, d);
   if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
   if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
-  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  const bool work = b > 0 && h > 0 && s_q > 0;
-  const int qs[4] = {b, h, s_q, d}, ks[4] = {b, h, s_kv, d};
   sdpa_status st;
+  if ((st = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st;
+  if ((st = check_heads(h, h_kv)) != SDPA_OK) return st;
+  const bool work = b > 0 && h > 0 && s_q > 0;
+  const int qs[4] = {b, h, s_q, d}, ks[4] = {b, h_kv, s_kv, d};
   if ((st = check_tensor("q", q, q_stride, qs, 4, dtype, work)) != SDPA_OK) return st;
   if ((st = check_tensor("o", o, o_stride, qs, 4, dtype, work)) != SDPA_OK) return st;
   if ((st = check_tensor("k", k, k_stride, ks, 4, dtype, work && s_kv > 0)) != SDPA_OK) return st;
@@ -149,32 +172,48 @@ sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float
   p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_ss = k_stride[2];
   p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_ss = v_stride[2];
   p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_ss = o_stride[2];
-  p.b = b; p.h = h; p.s_q = s_q; p.s_kv = s_kv;
+  p.b = b; p.h = h; p.h_kv = h_kv; p.s_q = s_q; p.s_kv = s_kv;
+  p.bottom_right = bottom_right; p.window_left = window_left;
   p.n_qtiles = (int)n_qtiles;
   p.scale_log2 = scale_log2(scale);
   p.negate_q = scale < 0.f;
   if (log_enabled())
-    fprintf(stderr, "[sdpa07] fwd dtype=%d b=%d h=%d s_q=%d s_kv=%d d=%d causal=%d grid=%lld\n",
-            (int)dtype, b, h, s_q, s_kv, d, causal, (long long)b * h * n_qtiles);
+    fprintf(stderr,
+            "[sdpa07] fwd dtype=%d b=%d h=%d h_kv=%d s_q=%d s_kv=%d d=%d causal=%d br=%d "
+            "window=%d\n",
+            (int)dtype, b, h, h_kv, s_q, s_kv, d, causal, bottom_right, window_left);
   return launch_status(sdpa07::launch_fwd(p, to_dt(dtype), d, causal != 0, false,
                                           (hipStream_t)stream),
                        "sdpa_fwd");
 }
 
-sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                            int num_seqs, int total_q, int total_kv, int max_seqlen_q,
-                            int max_seqlen_kv, sdpa_dtype dtype, int h, int d,
-                            const int64_t q_stride[3], const int64_t k_stride[3],
-                            const int64_t v_stride[3], const int64_t o_stride[3], float scale,
-                            int causal, void* stream) {
+sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     sdpa_dtype dtype, int b, int h, int s_q, int s_kv, int d,
+                     const int64_t q_stride[4], const int64_t k_stride[4],
+                     const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                     int causal, void* stream) {
+  return sdpa_fwd_ex(q, k, v, o, lse, dtype, b, h, h, s_q, s_kv, d, q_stride, k_stride, v_stride,
+                     o_stride, scale, causal, 0, -1, stream);
+}
+
+sdpa_status sdpa_fwd_varlen_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                               int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                               int max_seqlen_kv, sdpa_dtype dtype, int h, int h_kv, int d,
+                               const int64_t q_stride[3], const int64_t k_stride[3],
+                               const int64_t v_stride[3], const int64_t o_stride[3], float scale,
+                               int causal, int bottom_right, int window_left, void* stream) {
   if (!valid_dtype(dtype)) return fail(SDPA_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
   if (num_seqs < 0 || total_q < 0 || total_kv < 0 || h < 0 || d < 0 || max_seqlen_q < 0 ||
       max_seqlen_kv < 0)
     return fail(SDPA_ERR_INVALID_ARG, "negative size");
   if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
   if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
-  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  {
+    sdpa_status st0;
+    if ((st0 = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st0;
+    if ((st0 = check_heads(h, h_kv)) != SDPA_OK) return st0;
+  }
   const bool work = num_seqs > 0 && h > 0 && total_q > 0;
   if (work && (!cu_seqlens_q || !cu_seqlens_kv))
     return fail(SDPA_ERR_INVALID_ARG, "packed path needs cu_seqlens_q and cu_seqlens_kv");
@@ -183,7 +222,7 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
   if (work && max_seqlen_q > total_q)
     return fail(SDPA_ERR_INVALID_ARG, "max_seqlen_q %d exceeds total_q %d", max_seqlen_q,
                 total_q);
-  const int qs[3] = {total_q, h, d}, ks[3] = {total_kv, h, d};
+  const int qs[3] = {total_q, h, d}, ks[3] = {total_kv, h_kv, d};
   sdpa_status st;
   if ((st = check_tensor("q", q, q_stride, qs, 3, dtype, work)) != SDPA_OK) return st;
   if ((st = check_tensor("o", o, o_stride, qs, 3, dtype, work)) != SDPA_OK) return st;
@@ -206,7 +245,8 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
   p.k_ss = k_stride[0]; p.k_sh = k_stride[1];
   p.v_ss = v_stride[0]; p.v_sh = v_stride[1];
   p.o_ss = o_stride[0]; p.o_sh = o_stride[1];
-  p.b = num_seqs; p.h = h;
+  p.b = num_seqs; p.h = h; p.h_kv = h_kv;
+  p.bottom_right = bottom_right; p.window_left = window_left;
   p.n_qtiles = (int)n_qtiles;
   p.scale_log2 = scale_log2(scale);
   p.negate_q = scale < 0.f;
@@ -218,6 +258,18 @@ sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o
   return launch_status(sdpa07::launch_fwd(p, to_dt(dtype), d, causal != 0, true,
                                           (hipStream_t)stream),
                        "sdpa_fwd_varlen");
+}
+
+sdpa_status sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                            int max_seqlen_kv, sdpa_dtype dtype, int h, int d,
+                            const int64_t q_stride[3], const int64_t k_stride[3],
+                            const int64_t v_stride[3], const int64_t o_stride[3], float scale,
+                            int causal, void* stream) {
+  return sdpa_fwd_varlen_ex(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_kv, num_seqs, total_q,
+                            total_kv, max_seqlen_q, max_seqlen_kv, dtype, h, h, d, q_stride,
+                            k_stride, v_stride, o_stride, scale, causal, 0, -1, stream);
 }
 
 size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype) {

@@ -109,8 +109,8 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
     w.kv_len = max(k1 - k0, 0);
     w.q_off = (int64_t)q0 * p.q_ss + (int64_t)w.hi * p.q_sh;
     w.o_off = (int64_t)q0 * p.o_ss + (int64_t)w.hi * p.o_sh;
-    w.k_off = (int64_t)k0 * p.k_ss + (int64_t)w.hi * p.k_sh;
-    w.v_off = (int64_t)k0 * p.v_ss + (int64_t)w.hi * p.v_sh;
+    w.k_off = (int64_t)k0 * p.k_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)k0 * p.v_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
     w.lse_off = (int64_t)q0 * p.h + w.hi;
     w.lse_st = p.h;
   } else {
@@ -118,8 +118,8 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
     w.kv_len = p.s_kv;
     w.q_off = (int64_t)bi * p.q_sb + (int64_t)w.hi * p.q_sh;
     w.o_off = (int64_t)bi * p.o_sb + (int64_t)w.hi * p.o_sh;
-    w.k_off = (int64_t)bi * p.k_sb + (int64_t)w.hi * p.k_sh;
-    w.v_off = (int64_t)bi * p.v_sb + (int64_t)w.hi * p.v_sh;
+    w.k_off = (int64_t)bi * p.k_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)bi * p.v_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
     w.lse_off = ((int64_t)bi * p.h + w.hi) * p.s_q;
     w.lse_st = 1;
   }
@@ -166,15 +166,20 @@ __device__ __forceinline__ void mask_all(f32x16 (&s)[2]) {
     for (int r = 0; r < 16; ++r) s[mb][r] = -INFINITY;
 }
 
+// Hides the scores of keys outside the band of each row of a tile: key >
+// qi + shift (causal), key < qi + shift - window, key >= kv_len. shift = 0
+// (top-left) or kv_len - q_len (bottom-right); window is a huge value when
+// there is no left bound.
 template <bool CAUSAL>
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len,
-                                          int hf) {
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len, int hf,
+                                          int shift, int window) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kbase + s_key(mb, r, hf);
-      if ((CAUSAL && key > qi) || key >= kv_len) s[mb][r] = -INFINITY;
+      if ((CAUSAL && key > qi + shift) || key < qi + shift - window || key >= kv_len)
+        s[mb][r] = -INFINITY;
     }
 }
 
@@ -247,6 +252,7 @@ fwd16_kernel(FwdParams p) {
   constexpr int PASSES = CAUSAL ? 2 : 1;
   const int bh = blockIdx.x % nbh;
   const int bi = bh / p.h, hi = bh % p.h;
+  const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
   int q_len, kv_len;
   int64_t q_off, k_off, v_off, o_off, lse_off, lse_st;
   if constexpr (VARLEN) {
@@ -258,8 +264,8 @@ fwd16_kernel(FwdParams p) {
     kv_len = max(k1 - k0, 0);
     q_off = (int64_t)q0 * p.q_ss + (int64_t)hi * p.q_sh;
     o_off = (int64_t)q0 * p.o_ss + (int64_t)hi * p.o_sh;
-    k_off = (int64_t)k0 * p.k_ss + (int64_t)hi * p.k_sh;
-    v_off = (int64_t)k0 * p.v_ss + (int64_t)hi * p.v_sh;
+    k_off = (int64_t)k0 * p.k_ss + (int64_t)hk * p.k_sh;
+    v_off = (int64_t)k0 * p.v_ss + (int64_t)hk * p.v_sh;
     lse_off = (int64_t)q0 * p.h + hi;
     lse_st = p.h;
   } else {
@@ -267,11 +273,15 @@ fwd16_kernel(FwdParams p) {
     kv_len = p.s_kv;
     q_off = (int64_t)bi * p.q_sb + (int64_t)hi * p.q_sh;
     o_off = (int64_t)bi * p.o_sb + (int64_t)hi * p.o_sh;
-    k_off = (int64_t)bi * p.k_sb + (int64_t)hi * p.k_sh;
-    v_off = (int64_t)bi * p.v_sb + (int64_t)hi * p.v_sh;
+    k_off = (int64_t)bi * p.k_sb + (int64_t)hk * p.k_sh;
+    v_off = (int64_t)bi * p.v_sb + (int64_t)hk * p.v_sh;
     lse_off = ((int64_t)bi * p.h + hi) * p.s_q;
     lse_st = 1;
   }
+  // band of query row i: keys [i + shift - window, i + shift] (the upper
+  // bound only when causal), within [0, kv_len)
+  const int shift = p.bottom_right ? kv_len - q_len : 0;
+  const int window = p.window_left < 0 ? (1 << 29) : p.window_left;
   const T* __restrict__ Q = (const T*)p.q + q_off;
   const T* __restrict__ K = (const T*)p.k + k_off;
   const T* __restrict__ V = (const T*)p.v + v_off;
@@ -315,14 +325,24 @@ fwd16_kernel(FwdParams p) {
   const bool wave_active = row0 < q_len;
   const bool q_valid = wave_active && qi < q_len;
   const int last_q = min(q_len, (qt + 1) * BM) - 1;
-  const int kv_end = CAUSAL ? min(kv_len, last_q + 1) : kv_len;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // keys any row of the tile sees: [kv_begin, kv_end); the steps start at
+  // the tile pair holding kv_begin (step s covers tiles t0 + 2s, t0 + 2s + 1)
+  const int kv_end = CAUSAL ? min(kv_len, max(last_q + shift + 1, 0)) : kv_len;
+  const int kv_begin = min(kv_end, max(qt * BM + shift - window, 0));
+  const int t0 = kv_begin / (2 * BN) * 2;
+  const int n_tiles = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
   const int n_steps = (n_tiles + 1) / 2;  // two key tiles per step
-  const int wave_kv_end =
-      !wave_active ? 0 : (CAUSAL ? min(kv_len, min(q_len, row0 + 32)) : kv_len);
-  const int wave_tiles_all = (wave_kv_end + BN - 1) / BN;
-  // steps in which this wave has a key tile of its own (tile 2s + g)
-  const int wave_steps = wave_tiles_all > g ? (wave_tiles_all - g + 1) / 2 : 0;
+  // this wave's keys [wave_lo, wave_hi) and the steps in which its own tile
+  // (t0 + 2s + g) meets them: [wave_s0, wave_s1)
+  const int wave_last = min(row0 + 31, q_len - 1);
+  const int wave_hi = !wave_active ? 0 : (CAUSAL ? min(kv_len, max(wave_last + shift + 1, 0)) : kv_len);
+  const int wave_lo = min(wave_hi, max(row0 + shift - window, 0));
+  int wave_s0 = 0, wave_s1 = 0;
+  if (wave_hi > wave_lo) {
+    const int tlo = wave_lo / BN - t0, thi = (wave_hi + BN - 1) / BN - t0;  // tiles [tlo, thi)
+    wave_s0 = tlo > g ? (tlo - g + 1) / 2 : 0;
+    wave_s1 = thi > g ? (thi - g + 1) / 2 : 0;
+  }
 
   v8 qf[D / 16];
   f32x16 acc[D / 32];
@@ -354,7 +374,7 @@ fwd16_kernel(FwdParams p) {
   // built in scalar code outside the fused blocks
   auto tile_rsrc = [&](const T* __restrict__ base, int64_t stride, int t) -> i32x4 {
     const T* tb = base + (int64_t)t * BN * stride;
-    const int rows = t < 0 ? 0 : min(kv_end - t * BN, BN);
+    const int rows = t < t0 ? 0 : min(kv_end - t * BN, BN);
     const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
     const unsigned long long a = (unsigned long long)tb;
     return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
@@ -374,7 +394,7 @@ fwd16_kernel(FwdParams p) {
         vbuf0 + ((u + NBV) % NBV) * VBUF + XT(x) * TILE + RIT(x) * D);
   };
   auto rsrc2 = [&](const T* __restrict__ base, int64_t stride, int u) -> Rsrc2 {
-    return Rsrc2{{tile_rsrc(base, stride, 2 * u), tile_rsrc(base, stride, 2 * u + 1)}};
+    return Rsrc2{{tile_rsrc(base, stride, t0 + 2 * u), tile_rsrc(base, stride, t0 + 2 * u + 1)}};
   };
 
   // Softmax state (per lane = per query row; both halves agree):
@@ -568,14 +588,15 @@ fwd16_kernel(FwdParams p) {
     wait_vm(WaitStep{});
     __builtin_amdgcn_s_barrier();
     bool rescale = false;
-    if (s >= wave_steps) {
+    if (s < wave_s0 || s >= wave_s1) {
       mask_all(s_cur);
       a_cur = 1.f;
     } else {
-      const int kbase = (2 * s + g) * BN;  // this wave's current key tile
+      const int kbase = (t0 + 2 * s + g) * BN;  // this wave's current key tile
       float mx = mx_nxt;
-      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > kv_len) {
-        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf);
+      if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
+          kbase + BN > kv_len) {
+        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window);
         mx = row_max(s_cur);
       }
       rescale = decide(mx);
@@ -588,7 +609,7 @@ fwd16_kernel(FwdParams p) {
     }
   };
 
-  if (n_tiles > 0) {
+  if (n_steps > 0) {
     // Prologue: the query tile's 128 rows into LDS with the layout of one
     // step's two K tiles (rows past the sequence read as zeros), in the V
     // buffer that no load touches before block 0; then the loads that blocks
@@ -655,7 +676,7 @@ fwd16_kernel(FwdParams p) {
     // the P.V of the wave's tile of the last step, if it had one
     wait_vm(WaitStep{});
     __builtin_amdgcn_s_barrier();
-    if (wave_steps == n_steps) {
+    if (n_steps - 1 >= wave_s0 && n_steps - 1 < wave_s1) {
       const T* vb = vbuf0 + ((n_steps - 1) % NBV) * VBUF + g * TILE;
       if ((n_steps - 1) & 1) pv_only(vb, pb);
       else pv_only(vb, pa);
@@ -772,9 +793,16 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
   const bool q_valid = qi < w.q_len;
   const bool wave_active = row0 < w.q_len;
   const int blk_last_q = min(w.q_len, (w.qt + 1) * BM) - 1;
-  const int kv_end = CAUSAL ? min(w.kv_len, blk_last_q + 1) : w.kv_len;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = CAUSAL ? min(w.kv_len, min(w.q_len, row0 + 32)) : w.kv_len;
+  // band of row i: keys [i + shift - window, i + shift] (upper bound only
+  // when causal) within [0, kv_len); the tiles [j0, j1) cover the workgroup's
+  const int shift = p.bottom_right ? w.kv_len - w.q_len : 0;
+  const int window = p.window_left < 0 ? (1 << 29) : p.window_left;
+  const int kv_end = CAUSAL ? min(w.kv_len, max(blk_last_q + shift + 1, 0)) : w.kv_len;
+  const int kv_begin = min(kv_end, max(w.qt * BM + shift - window, 0));
+  const int j0 = kv_begin / BN, j1 = kv_end > kv_begin ? (kv_end + BN - 1) / BN : j0;
+  const int wave_last = min(row0 + 31, w.q_len - 1);
+  const int wave_kv_end = CAUSAL ? min(w.kv_len, max(wave_last + shift + 1, 0)) : w.kv_len;
+  const int wave_kv_begin = max(row0 + shift - window, 0);
 
   float qf[D / 2];
 #pragma unroll
@@ -814,17 +842,17 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
+  if (j1 > j0) {
+    load_tile(j0);
     store_tile(0);
   }
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+    if (j + 1 < j1) load_tile(j + 1);
     const int kbase = j * BN;
-    if (wave_active && kbase < wave_kv_end) {
+    if (wave_active && kbase < wave_kv_end && kbase + BN > wave_kv_begin) {
       f32x16 s[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -835,8 +863,9 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[ks], s[mb], 0, 0, 0);
         }
       }
-      if ((CAUSAL && kbase + BN - 1 > row0) || kbase + BN > w.kv_len)
-        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf);
+      if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
+          kbase + BN > w.kv_len)
+        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf, shift, window);
       const float alpha = softmax_tile(s, c, m_run, l_run);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
@@ -851,7 +880,7 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[mb][r], acc[db], 0, 0, 0);
           }
     }
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    if (j + 1 < j1) store_tile(buf ^ 1);
     __syncthreads();
   }
 

@@ -23,8 +23,11 @@ struct FwdParams {
   int64_t v_sb, v_sh, v_ss;
   int64_t o_sb, o_sh, o_ss;
   int b;          // batch (dense) or number of sequences (packed)
-  int h;
+  int h;          // query heads
+  int h_kv;       // key/value heads (h is a multiple; query head i reads K/V head i / (h / h_kv))
   int s_q, s_kv;  // dense lengths (unused when packed)
+  int bottom_right;  // 1: the diagonal of the band is aligned to the bottom-right corner
+  int window_left;   // keys kept left of the diagonal; < 0: no left bound
   int n_qtiles;   // query tiles per (b, h): ceil(s_q or max_seqlen_q / BM)
   float scale_log2;  // |scale| * log2(e)
   int negate_q;      // 1 when scale < 0 (the sign is moved onto Q, exactly)

@@ -30,8 +30,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for s in ("sdpa_fwd", "sdpa_fwd_varlen", "sdpa_bwd", "sdpa_bwd_workspace_size",
-              "sdpa_last_error", "sdpa_version"):
+    for s in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
+              "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_version"):
         assert s in syms
 
 
@@ -122,6 +122,53 @@ def test_varlen_validation(lib, kw, status, msg):
 def test_varlen_empty_batch_ok(lib):
     assert varlen(lib, cu_q=None, cu_kv=None, n=0) == OK
     assert varlen(lib, tq=0, maxq=0) == OK
+
+
+def fwd_ex(lib, h=2, h_kv=2, causal=1, br=0, window=-1, b=1, sq=8, skv=8, d=64, q=ALIGNED,
+           k=ALIGNED):
+    qs = dense_st(b, h, sq, d)
+    ks = dense_st(b, h_kv, skv, d)
+    return lib.sdpa_fwd_ex(q, k, ALIGNED, ALIGNED, None, BF16, b, h, h_kv, sq, skv, d, qs, ks, ks,
+                           qs, 0.125, causal, br, window, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(h=4, h_kv=3), INVALID, "multiple of h_kv"),
+    (dict(h=2, h_kv=0), INVALID, "multiple of h_kv"),
+    (dict(h_kv=-1), INVALID, "negative h_kv"),
+    (dict(h=2, h_kv=4), INVALID, "multiple of h_kv"),
+    (dict(br=1, causal=0, window=-1), INVALID, "bottom_right needs"),
+    (dict(br=2), INVALID, "bottom_right"),
+    (dict(window=-2), INVALID, "window_left"),
+    (dict(causal=3), INVALID, "causal"),
+])
+def test_fwd_ex_validation(lib, kw, status, msg):
+    assert fwd_ex(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(h=8, h_kv=2), dict(h=3, h_kv=1), dict(br=1, causal=1),
+                                dict(br=1, causal=0, window=4), dict(window=0),
+                                dict(causal=0, window=16)])
+def test_fwd_ex_accepts_valid_options_without_work(lib, kw):
+    # s_q = 0: every check passes and nothing is launched
+    assert fwd_ex(lib, sq=0, q=None, **kw) == OK
+
+
+def test_fwd_ex_checks_kv_shape_with_h_kv(lib):
+    # k is validated with h_kv heads: a NULL k with keys present is reported
+    assert fwd_ex(lib, h=4, h_kv=2, k=None) == INVALID
+    assert "k: NULL" in lib.sdpa_last_error().decode()
+
+
+def test_varlen_ex_validation(lib):
+    s = S3(2 * 64, 64, 1)
+    st = lib.sdpa_fwd_varlen_ex(ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, 2, 16,
+                                16, 8, 8, BF16, 4, 3, 64, s, s, s, s, 0.1, 1, 0, -1, None)
+    assert st == INVALID and "multiple of h_kv" in lib.sdpa_last_error().decode()
+    st = lib.sdpa_fwd_varlen_ex(ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, 2, 16,
+                                16, 8, 8, BF16, 2, 2, 64, s, s, s, s, 0.1, 0, 1, -1, None)
+    assert st == INVALID and "bottom_right needs" in lib.sdpa_last_error().decode()
 
 
 def test_bwd_workspace_size(lib):
