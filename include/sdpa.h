@@ -142,9 +142,10 @@ sdpa_status sdpa_fwd_varlen_ex(const void* q, const void* k, const void* v, void
                                int causal, int bottom_right, int window_left, void* stream);
 
 /*
- * Bytes of device workspace sdpa_bwd needs for these sizes: two fp32 values
- * per query row (rowsum(dO * O) and the statistic in base 2), rounded up to
- * 256 bytes. The caller allocates it (256-byte aligned).
+ * Bytes of device workspace the backward needs for these sizes: two fp32
+ * values per query row (rowsum(dO * O) and the statistic in base 2), rounded
+ * up to 256 bytes. The caller allocates it (256-byte aligned). For the packed
+ * backward pass b = 1, s_q = total_q.
  */
 size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype);
 
@@ -170,6 +171,56 @@ sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
                      const int64_t o_stride[4], const int64_t do_stride[4],
                      const int64_t dq_stride[4], const int64_t dk_stride[4],
                      const int64_t dv_stride[4], float scale, int causal, void* stream);
+
+/*
+ * Dense backward with grouped-query heads and the band options; the mask
+ * arguments are those of sdpa_fwd_ex and must match the forward call that
+ * produced o and lse.
+ *   k, v, dk, dv are (b, h_kv, s_kv, d); dK and dV of K/V head j sum the
+ *   contributions of query heads j * (h / h_kv) .. (j + 1) * (h / h_kv) - 1.
+ *   Keys no query sees get dK = dV = 0; queries that see no key get dQ = 0.
+ * Row strides must keep a 128-row tile within 2 GiB (SDPA_ERR_UNSUPPORTED).
+ * Cited: cudnn-frontend PR #554 (the sdpa backward takes the forward's mask
+ * options; GQA support in the provider); the cuDNN Graph API article,
+ * section 5 (the band mask).
+ */
+sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
+                        int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                        const int64_t k_stride[4], const int64_t v_stride[4],
+                        const int64_t o_stride[4], const int64_t do_stride[4],
+                        const int64_t dq_stride[4], const int64_t dk_stride[4],
+                        const int64_t dv_stride[4], float scale, int causal, int bottom_right,
+                        int window_left, void* stream);
+
+/*
+ * Packed THD backward (fp16/bf16), with grouped-query heads and the band
+ * options as sdpa_bwd_ex.
+ *   q, o, dout, dq: (total_q, h, d); k, v, dk, dv: (total_kv, h_kv, d); each
+ *     with its own (token, head) strides and d stride 1;
+ *   lse: fp32 (total_q, h) token-major, as written by sdpa_fwd_varlen(_ex);
+ *   cu_seqlens_q / cu_seqlens_kv, num_seqs, total_*, max_seqlen_*: as in
+ *     sdpa_fwd_varlen (device int32 arrays of num_seqs + 1 entries;
+ *     max_seqlen_* must be at least every sequence's length);
+ *   workspace: sdpa_bwd_workspace_size(1, h, total_q, d, dtype) bytes.
+ * Rows at or past total_q / total_kv are never read or written; rows of
+ * sequences with no keys get dQ = 0, rows of sequences with no queries
+ * get dK = dV = 0. Deterministic (no atomics).
+ * Cited: cudnn-frontend PR #554 (THD packing with cu_seqlens and max_seqlen,
+ * the (T, H, 1) token-major statistic shared by forward and backward).
+ */
+sdpa_status sdpa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                            int max_seqlen_kv, void* workspace, size_t workspace_bytes,
+                            sdpa_dtype dtype, int h, int h_kv, int d, const int64_t q_stride[3],
+                            const int64_t k_stride[3], const int64_t v_stride[3],
+                            const int64_t o_stride[3], const int64_t do_stride[3],
+                            const int64_t dq_stride[3], const int64_t dk_stride[3],
+                            const int64_t dv_stride[3], float scale, int causal,
+                            int bottom_right, int window_left, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* sdpa_last_error(void);

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI, minus the ``sdpa_`` prefix; the
   fwd(q, k, v, ...)                       dense forward, returns (o, lse)
   fwd_varlen(q, k, v, cu_q, cu_kv, ...)   packed THD forward, returns (o, lse)
   bwd(q, k, v, o, dout, lse, ...)         dense backward, returns (dq, dk, dv)
+  bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_kv, ...)
+                                          packed THD backward, returns (dq, dk, dv)
 Options: grouped-query heads (k, v with fewer heads than q), causal,
 bottom_right (diagonal aligned to the bottom-right corner), window_left.
 """
@@ -27,7 +29,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "bwd", "bwd_workspace_size", "last_error", "version",
+__all__ = ["fwd", "fwd_varlen", "bwd", "bwd_varlen", "bwd_workspace_size", "last_error", "version",
            "library_path", "SdpaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,7 +72,12 @@ def _load():
     lib.sdpa_bwd_workspace_size.restype = Z
     lib.sdpa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I,
                              S4, S4, S4, S4, S4, S4, S4, S4, F, I, P]
-    for f in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd"):
+    lib.sdpa_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I,
+                                S4, S4, S4, S4, S4, S4, S4, S4, F, I, I, I, P]
+    lib.sdpa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, Z, I, I,
+                                    I, I, S3, S3, S3, S3, S3, S3, S3, S3, F, I, I, I, P]
+    for f in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
+              "sdpa_bwd_ex", "sdpa_bwd_varlen"):
         getattr(lib, f).restype = I
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.restype = ctypes.c_char_p
@@ -212,14 +219,21 @@ def bwd_workspace_size(b: int, h: int, s_q: int, d: int, dtype: torch.dtype) -> 
 
 
 def bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
-        dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Dense backward. Returns (dq, dk, dv), each shaped and strided like q, k, v by default."""
+        bottom_right: bool = False, window_left: int = -1, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Dense backward. Returns (dq, dk, dv), each shaped and strided like q, k, v by default.
+
+    The mask options must be those of the forward that produced o and lse; k, v
+    may have fewer heads than q (dk, dv then sum over each head group).
+    """
     lib = _load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("dense path expects 4-D (b, h, s, d) tensors")
     b, h, s_q, d = q.shape
-    s_kv = k.shape[2]
+    h_kv, s_kv = k.shape[1], k.shape[2]
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
         raise ValueError("o and dout must have q's shape")
-    if tuple(k.shape) != (b, h, s_kv, d) or tuple(v.shape) != (b, h, s_kv, d):
+    if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
         raise ValueError("k/v shape mismatch")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, h, s_q):
         raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
@@ -231,11 +245,67 @@ def bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = 
     if workspace is None:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    st = lib.sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                      _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                      _dtype_code(q), b, h, s_q, s_kv, d, _strides(q, 4), _strides(k, 4),
-                      _strides(v, 4), _strides(o, 4), _strides(dout, 4), _strides(dq, 4),
-                      _strides(dk, 4), _strides(dv, 4), scale, int(bool(causal)),
-                      _stream(stream))
+    st = lib.sdpa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _dtype_code(q), b, h,
+                         h_kv, s_q, s_kv, d, _strides(q, 4), _strides(k, 4), _strides(v, 4),
+                         _strides(o, 4), _strides(dout, 4), _strides(dq, 4), _strides(dk, 4),
+                         _strides(dv, 4), scale, int(bool(causal)), int(bool(bottom_right)),
+                         int(window_left), _stream(stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q: torch.Tensor, cu_seqlens_kv: torch.Tensor,
+               max_seqlen_q: int, max_seqlen_kv: int, *, total_q: Optional[int] = None,
+               total_kv: Optional[int] = None, scale: Optional[float] = None,
+               causal: bool = False, bottom_right: bool = False, window_left: int = -1,
+               dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Packed THD backward: q, o, dout (T_q, h, d), k, v (T_kv, h_kv, d), lse fp32
+    (T_q, h) token-major from fwd_varlen, int32 cu_seqlens on the device.
+
+    Returns (dq, dk, dv) shaped like q, k, v; rows past total_q / total_kv are
+    left untouched.
+    """
+    lib = _load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed path expects (T, h, d) tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_kv.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.shape != cu_seqlens_kv.shape or cu_seqlens_q.dim() != 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must be 1-D of the same length")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_kv.is_contiguous()):
+        raise ValueError("cu_seqlens must be contiguous")
+    t_q, h, d = q.shape
+    t_kv, h_kv = k.shape[0], k.shape[1]
+    if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k, v")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    _same_dtype(q, k, v, o, dout, dq, dk, dv)
+    total_q = t_q if total_q is None else int(total_q)
+    total_kv = t_kv if total_kv is None else int(total_kv)
+    if total_q > t_q or total_kv > t_kv:
+        raise ValueError("total_q/total_kv exceed the tensors' first dimension")
+    if (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.dim() != 2
+            or lse.shape[1] != h or lse.shape[0] < total_q):
+        raise ValueError("lse must be a contiguous float32 (T_q, h) tensor")
+    n = cu_seqlens_q.shape[0] - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = bwd_workspace_size(1, h, total_q, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.sdpa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_kv), n, total_q, total_kv, int(max_seqlen_q),
+                             int(max_seqlen_kv), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _dtype_code(q), h,
+                             h_kv, d, _strides(q, 3), _strides(k, 3), _strides(v, 3),
+                             _strides(o, 3), _strides(dout, 3), _strides(dq, 3),
+                             _strides(dk, 3), _strides(dv, 3), scale, int(bool(causal)),
+                             int(bool(bottom_right)), int(window_left), _stream(stream))
     _check(st)
     return dq, dk, dv

@@ -128,6 +128,18 @@ sdpa_status check_heads(int h, int h_kv) {
   return SDPA_OK;
 }
 
+// Workspace checks shared by both backward entry points.
+sdpa_status check_workspace(const void* workspace, size_t workspace_bytes, long long rows) {
+  if (!workspace) return fail(SDPA_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SDPA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const size_t need = sdpa07::bwd_workspace_bytes(rows);
+  if (workspace_bytes < need)
+    return fail(SDPA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  return SDPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,14 +291,15 @@ size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype) {
   return sdpa07::bwd_workspace_bytes((long long)b * h * s_q);
 }
 
-sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
-                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
-                     int s_q, int s_kv, int d, const int64_t q_stride[4],
-                     const int64_t k_stride[4], const int64_t v_stride[4],
-                     const int64_t o_stride[4], const int64_t do_stride[4],
-                     const int64_t dq_stride[4], const int64_t dk_stride[4],
-                     const int64_t dv_stride[4], float scale, int causal, void* stream) {
+sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
+                        int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                        const int64_t k_stride[4], const int64_t v_stride[4],
+                        const int64_t o_stride[4], const int64_t do_stride[4],
+                        const int64_t dq_stride[4], const int64_t dk_stride[4],
+                        const int64_t dv_stride[4], float scale, int causal, int bottom_right,
+                        int window_left, void* stream) {
   if (!valid_dtype(dtype)) return fail(SDPA_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
   if (dtype == SDPA_FP32)
     return fail(SDPA_ERR_UNSUPPORTED, "backward supports fp16 and bf16 io only");
@@ -294,11 +307,12 @@ sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
     return fail(SDPA_ERR_INVALID_ARG, "negative size");
   if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
   if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
-  if (causal != 0 && causal != 1) return fail(SDPA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  sdpa_status st;
+  if ((st = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st;
+  if ((st = check_heads(h, h_kv)) != SDPA_OK) return st;
   const bool work = b > 0 && h > 0 && (s_q > 0 || s_kv > 0);
   const bool qwork = work && s_q > 0, kwork = work && s_kv > 0;
-  const int qs[4] = {b, h, s_q, d}, ks[4] = {b, h, s_kv, d};
-  sdpa_status st;
+  const int qs[4] = {b, h, s_q, d}, ks[4] = {b, h_kv, s_kv, d};
   if ((st = check_tensor("q", q, q_stride, qs, 4, dtype, qwork && kwork)) != SDPA_OK) return st;
   if ((st = check_tensor("o", o, o_stride, qs, 4, dtype, qwork && kwork)) != SDPA_OK) return st;
   if ((st = check_tensor("dout", dout, do_stride, qs, 4, dtype, qwork && kwork)) != SDPA_OK)
@@ -308,16 +322,15 @@ sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
   if ((st = check_tensor("v", v, v_stride, ks, 4, dtype, qwork && kwork)) != SDPA_OK) return st;
   if ((st = check_tensor("dk", dk, dk_stride, ks, 4, dtype, kwork)) != SDPA_OK) return st;
   if ((st = check_tensor("dv", dv, dv_stride, ks, 4, dtype, kwork)) != SDPA_OK) return st;
+  if ((st = check_tile_span("q", q_stride[2], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("dout", do_stride[2], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("k", k_stride[2], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("v", v_stride[2], dtype)) != SDPA_OK) return st;
   if (qwork && kwork && !lse)
     return fail(SDPA_ERR_INVALID_ARG, "lse (the forward's statistic) is required");
-  if (qwork && kwork) {
-    if (!workspace) return fail(SDPA_ERR_INVALID_ARG, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-      return fail(SDPA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    if (workspace_bytes < sdpa_bwd_workspace_size(b, h, s_q, d, dtype))
-      return fail(SDPA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
-                  workspace_bytes, sdpa_bwd_workspace_size(b, h, s_q, d, dtype));
-  }
+  if (qwork && kwork &&
+      (st = check_workspace(workspace, workspace_bytes, (long long)b * h * s_q)) != SDPA_OK)
+    return st;
   const long long tq = (s_q + sdpa07::kBwdBlockM - 1) / sdpa07::kBwdBlockM;
   const long long tk = (s_kv + sdpa07::kBwdBlockN - 1) / sdpa07::kBwdBlockN;
   if ((long long)b * h * (tq > tk ? tq : tk) > 0x7fffffffLL)
@@ -336,13 +349,116 @@ sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
   p.dk_sb = dk_stride[0]; p.dk_sh = dk_stride[1]; p.dk_ss = dk_stride[2];
   p.dv_sb = dv_stride[0]; p.dv_sh = dv_stride[1]; p.dv_ss = dv_stride[2];
   p.b = b; p.h = h; p.s_q = s_q; p.s_kv = s_kv;
+  p.h_kv = h_kv; p.bottom_right = bottom_right; p.window_left = window_left;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   if (log_enabled())
-    fprintf(stderr, "[sdpa07] bwd dtype=%d b=%d h=%d s_q=%d s_kv=%d d=%d causal=%d\n",
-            (int)dtype, b, h, s_q, s_kv, d, causal);
-  return launch_status(sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, (hipStream_t)stream),
-                       "sdpa_bwd");
+    fprintf(stderr,
+            "[sdpa07] bwd dtype=%d b=%d h=%d h_kv=%d s_q=%d s_kv=%d d=%d causal=%d br=%d "
+            "window=%d\n",
+            (int)dtype, b, h, h_kv, s_q, s_kv, d, causal, bottom_right, window_left);
+  return launch_status(
+      sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, false, (hipStream_t)stream),
+      "sdpa_bwd");
+}
+
+sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
+                     int s_q, int s_kv, int d, const int64_t q_stride[4],
+                     const int64_t k_stride[4], const int64_t v_stride[4],
+                     const int64_t o_stride[4], const int64_t do_stride[4],
+                     const int64_t dq_stride[4], const int64_t dk_stride[4],
+                     const int64_t dv_stride[4], float scale, int causal, void* stream) {
+  return sdpa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, dtype, b, h,
+                     h, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride, do_stride,
+                     dq_stride, dk_stride, dv_stride, scale, causal, 0, -1, stream);
+}
+
+sdpa_status sdpa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                            int max_seqlen_kv, void* workspace, size_t workspace_bytes,
+                            sdpa_dtype dtype, int h, int h_kv, int d, const int64_t q_stride[3],
+                            const int64_t k_stride[3], const int64_t v_stride[3],
+                            const int64_t o_stride[3], const int64_t do_stride[3],
+                            const int64_t dq_stride[3], const int64_t dk_stride[3],
+                            const int64_t dv_stride[3], float scale, int causal,
+                            int bottom_right, int window_left, void* stream) {
+  if (!valid_dtype(dtype)) return fail(SDPA_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
+  if (dtype == SDPA_FP32)
+    return fail(SDPA_ERR_UNSUPPORTED, "backward supports fp16 and bf16 io only");
+  if (num_seqs < 0 || total_q < 0 || total_kv < 0 || h < 0 || d < 0 || max_seqlen_q < 0 ||
+      max_seqlen_kv < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "negative size");
+  if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
+  sdpa_status st;
+  if ((st = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st;
+  if ((st = check_heads(h, h_kv)) != SDPA_OK) return st;
+  const bool work = num_seqs > 0 && h > 0 && (total_q > 0 || total_kv > 0);
+  const bool qwork = work && total_q > 0, kwork = work && total_kv > 0;
+  if (work && (!cu_seqlens_q || !cu_seqlens_kv))
+    return fail(SDPA_ERR_INVALID_ARG, "packed path needs cu_seqlens_q and cu_seqlens_kv");
+  if ((qwork && max_seqlen_q <= 0) || (kwork && max_seqlen_kv <= 0))
+    return fail(SDPA_ERR_INVALID_ARG, "packed path needs max_seqlen_q > 0 and max_seqlen_kv > 0");
+  if ((work && max_seqlen_q > total_q) || (work && max_seqlen_kv > total_kv))
+    return fail(SDPA_ERR_INVALID_ARG, "max_seqlen (%d, %d) exceeds the totals (%d, %d)",
+                max_seqlen_q, max_seqlen_kv, total_q, total_kv);
+  const int qs[3] = {total_q, h, d}, ks[3] = {total_kv, h_kv, d};
+  if ((st = check_tensor("q", q, q_stride, qs, 3, dtype, qwork && kwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, qs, 3, dtype, qwork && kwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("dout", dout, do_stride, qs, 3, dtype, qwork && kwork)) != SDPA_OK)
+    return st;
+  if ((st = check_tensor("dq", dq, dq_stride, qs, 3, dtype, qwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, ks, 3, dtype, qwork && kwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("v", v, v_stride, ks, 3, dtype, qwork && kwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_stride, ks, 3, dtype, kwork)) != SDPA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_stride, ks, 3, dtype, kwork)) != SDPA_OK) return st;
+  if ((st = check_tile_span("q", q_stride[0], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("dout", do_stride[0], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("k", k_stride[0], dtype)) != SDPA_OK) return st;
+  if ((st = check_tile_span("v", v_stride[0], dtype)) != SDPA_OK) return st;
+  if (qwork && kwork && !lse)
+    return fail(SDPA_ERR_INVALID_ARG, "lse (the forward's statistic) is required");
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
+  if (qwork && kwork &&
+      (st = check_workspace(workspace, workspace_bytes, (long long)total_q * h)) != SDPA_OK)
+    return st;
+  const long long tq = (max_seqlen_q + sdpa07::kBwdBlockM - 1) / sdpa07::kBwdBlockM;
+  const long long tk = (max_seqlen_kv + sdpa07::kBwdBlockN - 1) / sdpa07::kBwdBlockN;
+  if ((long long)num_seqs * h * (tq > tk ? tq : tk) > 0x7fffffffLL)
+    return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
+  if (!work) return ok();
+
+  sdpa07::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.delta = (float*)workspace;
+  p.q_ss = q_stride[0]; p.q_sh = q_stride[1];
+  p.k_ss = k_stride[0]; p.k_sh = k_stride[1];
+  p.v_ss = v_stride[0]; p.v_sh = v_stride[1];
+  p.o_ss = o_stride[0]; p.o_sh = o_stride[1];
+  p.do_ss = do_stride[0]; p.do_sh = do_stride[1];
+  p.dq_ss = dq_stride[0]; p.dq_sh = dq_stride[1];
+  p.dk_ss = dk_stride[0]; p.dk_sh = dk_stride[1];
+  p.dv_ss = dv_stride[0]; p.dv_sh = dv_stride[1];
+  p.b = num_seqs; p.h = h; p.s_q = max_seqlen_q; p.s_kv = max_seqlen_kv;
+  p.h_kv = h_kv; p.bottom_right = bottom_right; p.window_left = window_left;
+  p.cu_q = cu_seqlens_q; p.cu_kv = cu_seqlens_kv;
+  p.total_q = total_q; p.total_kv = total_kv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (log_enabled())
+    fprintf(stderr,
+            "[sdpa07] bwd_varlen dtype=%d n=%d h=%d h_kv=%d T_q=%d T_kv=%d max_q=%d max_kv=%d "
+            "d=%d causal=%d br=%d window=%d\n",
+            (int)dtype, num_seqs, h, h_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, d,
+            causal, bottom_right, window_left);
+  return launch_status(
+      sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, true, (hipStream_t)stream),
+      "sdpa_bwd_varlen");
 }
 
 }  // extern "C"

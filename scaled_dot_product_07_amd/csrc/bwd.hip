@@ -14,11 +14,13 @@
 //   bwd_pre   D = rowsum(dO * O) and LSE in base 2 (LSE * log2 e; +inf for a
 //             row without visible keys so that its P is 0), one pass over
 //             dO and O;
-//   bwd_dkdv  one wave per 32 keys: its K and V rows stay in VGPRs as MFMA B
-//             operands, and 64-query tiles of Q, dO (with their LSE and D)
-//             stream through double-buffered LDS. Per tile: S = Q K^T and
-//             dP = dO V^T (the lane owns one key column), P and dS in VGPRs,
-//             then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//   bwd_dkdv  one wave per 32 keys of one K/V head: its K and V rows stay in
+//             VGPRs as MFMA B operands, and 64-query tiles of Q, dO (with
+//             their LSE and D) of every query head that reads this K/V head
+//             stream through double-buffered LDS, so dK and dV sum over the
+//             head group in registers. Per tile: S = Q K^T and dP = dO V^T
+//             (the lane owns one key column), P and dS in VGPRs, then
+//             dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 //             through the transposing LDS read ds_read_b64_tr_b16;
 //   bwd_dq    one wave per 32 queries: its Q and dO rows stay in VGPRs, and
 //             64-key tiles of K, V stream through LDS. Per tile: S^T = K Q^T
@@ -26,8 +28,17 @@
 //             dQ^T += K^T dS^T.
 // The contraction index of the second products is relabelled exactly as in
 // the forward (P, dS go from the MFMA C layout to B operands in registers).
-// Causal (top-left) masking skips fully hidden tiles and masks the diagonal
-// ones; rows past the sequence read as zeros through buffer bounds.
+//
+// Masking follows the forward's band (cudnn-frontend PR #554's sdpa API:
+// is_causal, causal_bottom_right, window_left): query i of a sequence with
+// s_q queries and s_kv keys sits on diagonal key p = i (+ s_kv - s_q when
+// aligned bottom-right) and sees keys p - W .. p (no upper bound without
+// causal, no lower one without a window). Each workgroup visits only the
+// tiles that intersect the band, each wave skips the tiles its rows or keys
+// do not reach, and element masks run only on tiles the band cuts. Query
+// head i reads K/V head i / (h / h_kv). The packed (THD) variant takes each
+// sequence's lengths from cu_seqlens; its statistic and workspace rows are
+// token-major (token * h + head).
 
 #include "kernel_common.h"
 #include "sdpa_internal.h"
@@ -42,32 +53,76 @@ constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave)
 constexpr int kDkdvQ = 64;      // queries per streamed tile
 constexpr int kDqRows = 128;    // queries per dQ workgroup (32 per wave)
 constexpr int kDqK = 64;        // keys per streamed tile
+constexpr int kNoWindow = 1 << 29;  // window_left = -1: a left bound no key reaches
 
 template <typename T>
 __device__ __forceinline__ float to_f(T x) {
   return (float)x;
 }
 
+// Rows of one batch entry (dense) or one packed sequence (THD): lengths and
+// the element offsets of its row 0 for a given head. Packed bounds are
+// clamped to [0, total) so rows past the packed totals are never touched.
+template <bool VARLEN>
+struct Seq {
+  int bi, q0, k0, q_len, kv_len;
+  __device__ Seq(const BwdParams& p, int b) : bi(b) {
+    if constexpr (VARLEN) {
+      q0 = min(max(p.cu_q[b], 0), p.total_q);
+      const int q1 = min(max(p.cu_q[b + 1], 0), p.total_q);
+      k0 = min(max(p.cu_kv[b], 0), p.total_kv);
+      const int k1 = min(max(p.cu_kv[b + 1], 0), p.total_kv);
+      q_len = max(q1 - q0, 0);
+      kv_len = max(k1 - k0, 0);
+    } else {
+      q0 = k0 = 0;
+      q_len = p.s_q;
+      kv_len = p.s_kv;
+    }
+  }
+  __device__ int64_t qoff(int64_t sb, int64_t sh, int64_t ss, int hd) const {
+    return (VARLEN ? (int64_t)q0 * ss : (int64_t)bi * sb) + (int64_t)hd * sh;
+  }
+  __device__ int64_t koff(int64_t sb, int64_t sh, int64_t ss, int hd) const {
+    return (VARLEN ? (int64_t)k0 * ss : (int64_t)bi * sb) + (int64_t)hd * sh;
+  }
+  // index of query row 0 of head hd in the statistic / workspace rows, and
+  // the step between consecutive query rows
+  __device__ int64_t st0(const BwdParams& p, int hd) const {
+    return VARLEN ? (int64_t)q0 * p.h + hd : ((int64_t)bi * p.h + hd) * p.s_q;
+  }
+  static __device__ int st_step(const BwdParams& p) { return VARLEN ? p.h : 1; }
+};
+
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) in fp32 and LSE in base 2. D/8 lanes per row.
-template <typename T, int D>
-__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2) {
+// D = rowsum(dO * O) in fp32 and LSE in base 2, row r of the statistic's
+// layout ((b, h, s_q) dense, (token, h) packed). D/8 lanes per row.
+template <typename T, int D, bool VARLEN>
+__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2,
+                                                               long long n) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int RPB = kPreThreads / LPR;
   const int tid = threadIdx.x;
   const long long r = (long long)blockIdx.x * RPB + tid / LPR;
-  const long long n = (long long)p.b * p.h * p.s_q;
   const int sub = tid % LPR;
   float acc = 0.f;
   if (r < n) {
-    const int si = (int)(r % p.s_q);
-    const long long bh = r / p.s_q;
-    const int hi = (int)(bh % p.h), bi = (int)(bh / p.h);
-    const T* o = (const T*)p.o + bi * p.o_sb + hi * p.o_sh + (long long)si * p.o_ss + sub * 8;
-    const T* g =
-        (const T*)p.dout + bi * p.do_sb + hi * p.do_sh + (long long)si * p.do_ss + sub * 8;
+    int64_t oo, go;
+    if constexpr (VARLEN) {
+      const long long tok = r / p.h;
+      const int hi = (int)(r % p.h);
+      oo = tok * p.o_ss + hi * p.o_sh;
+      go = tok * p.do_ss + hi * p.do_sh;
+    } else {
+      const int si = (int)(r % p.s_q);
+      const long long bh = r / p.s_q;
+      const int hi = (int)(bh % p.h), bi = (int)(bh / p.h);
+      oo = bi * p.o_sb + hi * p.o_sh + (long long)si * p.o_ss;
+      go = bi * p.do_sb + hi * p.do_sh + (long long)si * p.do_ss;
+    }
     typedef T t8 __attribute__((ext_vector_type(8)));
-    const t8 ov = *(const t8*)o, gv = *(const t8*)g;
+    const t8 ov = *(const t8*)((const T*)p.o + oo + sub * 8);
+    const t8 gv = *(const t8*)((const T*)p.dout + go + sub * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(to_f(ov[e]), to_f(gv[e]), acc);
   }
@@ -141,7 +196,7 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   constexpr int BQ = kDkdvQ, PITCH = D + 8;
   using M = Mfma16<T>;
@@ -152,31 +207,32 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
   __shared__ __attribute__((aligned(16))) float l2l[2][BQ];
   __shared__ __attribute__((aligned(16))) float dll[2][BQ];
 
-  const int nbh = p.b * p.h;
+  const int nbh = p.b * p.h_kv;
   const int kt = blockIdx.x / nbh;  // key tile; the first ones see the most queries
   const int bh = blockIdx.x % nbh;
-  const int bi = bh / p.h, hi = bh % p.h;
+  const int bi = bh / p.h_kv, hk = bh % p.h_kv;
+  const int group = p.h / p.h_kv;  // query heads hk * group .. + group - 1 read this K/V head
+  const Seq<VARLEN> sq(p, bi);
+  if (kt * kDkdvKeys >= sq.kv_len) return;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hf = lane / 32, col = lane % 32;
   const int key0 = kt * kDkdvKeys + wave * 32;  // first key of this wave
   const int kj = key0 + col;                     // this lane's key
-  if (kt * kDkdvKeys >= p.s_kv) return;
+  const int shift = p.bottom_right ? sq.kv_len - sq.q_len : 0;
+  const int window = p.window_left < 0 ? kNoWindow : p.window_left;
 
-  const T* Q = (const T*)p.q + bi * p.q_sb + hi * p.q_sh;
-  const T* G = (const T*)p.dout + bi * p.do_sb + hi * p.do_sh;
-  const T* K = (const T*)p.k + bi * p.k_sb + hi * p.k_sh;
-  const T* V = (const T*)p.v + bi * p.v_sb + hi * p.v_sh;
-  const float* L2 = lse2 + (int64_t)bh * p.s_q;
-  const float* DL = p.delta + (int64_t)bh * p.s_q;
+  const T* K = (const T*)p.k + sq.koff(p.k_sb, p.k_sh, p.k_ss, hk);
+  const T* V = (const T*)p.v + sq.koff(p.v_sb, p.v_sh, p.v_ss, hk);
   const float c = p.scale_log2;
+  const int st_step = Seq<VARLEN>::st_step(p);
 
   // this lane's K and V rows as B operands (B[k = d][n = key])
   v8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     i16x8 a = {}, b = {};
-    if (kj < p.s_kv) {
+    if (kj < sq.kv_len) {
       a = *(const i16x8*)(K + (int64_t)kj * p.k_ss + 16 * ks + 8 * hf);
       b = *(const i16x8*)(V + (int64_t)kj * p.v_ss + 16 * ks + 8 * hf);
     }
@@ -190,22 +246,38 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
     dv[db] = f32x16{};
   }
 
-  const int n_qt = (p.s_q + BQ - 1) / BQ;
-  const int t0 = CAUSAL ? min(kt * kDkdvKeys / BQ, n_qt) : 0;  // first tile with a visible query
-  const int wave_t0 = CAUSAL ? key0 / BQ : 0;
+  // Query rows that see a key of this workgroup: i + shift >= first key
+  // (causal) and i + shift - window <= last key.
+  const int key_hi = min(sq.kv_len, kt * kDkdvKeys + kDkdvKeys) - 1;
+  const int i_lo = CAUSAL ? max(kt * kDkdvKeys - shift, 0) : 0;
+  const int i_hi = min(sq.q_len - 1, key_hi - shift + window);
+  const int t_lo = i_lo / BQ;
+  const int nt = i_hi >= i_lo ? i_hi / BQ + 1 - t_lo : 0;  // query tiles per head
+  // the tiles this wave's keys reach (inclusive bounds)
+  const int wt_lo = CAUSAL ? max(key0 - shift, 0) / BQ : 0;
+  const int wi_hi = min(key0 + 31, sq.kv_len - 1) - shift + window;
+  const int wt_hi = key0 < sq.kv_len && wi_hi >= 0 ? wi_hi / BQ : -1;
+
+  // iteration it covers query head hk * group + it / nt, tile t_lo + it % nt
+  const int n_it = group * nt;
   LQ lq, lg;
   lq.init(tid, p.q_ss, PITCH);
   lg.init(tid, p.do_ss, PITCH);
   i16x8 qr[LQ::CPT], gr[LQ::CPT];
   float l2r = 0.f, dlr = 0.f;
-  auto gload = [&](int t) {
-    const int rows = p.s_q - t * BQ;
-    lq.load(qr, Q + (int64_t)t * BQ * p.q_ss, rows);
-    lg.load(gr, G + (int64_t)t * BQ * p.do_ss, rows);
+  auto gload = [&](int it) {
+    const int hq = hk * group + it / nt, t = t_lo + it % nt;
+    const int rows = sq.q_len - t * BQ;
+    lq.load(qr, (const T*)p.q + sq.qoff(p.q_sb, p.q_sh, p.q_ss, hq) + (int64_t)t * BQ * p.q_ss,
+            rows);
+    lg.load(gr,
+            (const T*)p.dout + sq.qoff(p.do_sb, p.do_sh, p.do_ss, hq) + (int64_t)t * BQ * p.do_ss,
+            rows);
     if (tid < BQ) {
       const int qrow = t * BQ + tid;
-      l2r = qrow < p.s_q ? L2[qrow] : INFINITY;
-      dlr = qrow < p.s_q ? DL[qrow] : 0.f;
+      const int64_t si = sq.st0(p, hq) + (int64_t)qrow * st_step;
+      l2r = qrow < sq.q_len ? lse2[si] : INFINITY;
+      dlr = qrow < sq.q_len ? p.delta[si] : 0.f;
     }
   };
   auto lstore = [&](int buf) {
@@ -219,15 +291,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
-  if (t0 < n_qt) {
-    gload(t0);
+  if (n_it > 0) {
+    gload(0);
     lstore(0);
   }
   __syncthreads();
-  for (int t = t0; t < n_qt; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < n_qt) gload(t + 1);
-    if (t >= wave_t0) {
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_it) gload(it + 1);
+    const int t = t_lo + it % nt;
+    if (t >= wt_lo && t <= wt_hi) {
       const T* qb_ = ql[buf];
       const T* gb_ = gl[buf];
       f32x16 s[2], dp[2];
@@ -244,8 +317,11 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
         }
       }
       // P and dS in the C layout: lane = key kj, register r of block qb =
-      // query t*BQ + 32qb + 8(r/4) + 4hf + r%4
-      const bool mask = CAUSAL && t * BQ < key0 + 31;
+      // query t*BQ + 32qb + 8(r/4) + 4hf + r%4. The band cuts this tile if
+      // its first query hides the wave's last key (causal) or its last
+      // query hides the wave's first key (window).
+      const bool mask = (CAUSAL && key0 + 31 > t * BQ + shift) ||
+                        key0 < t * BQ + BQ - 1 + shift - window;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -258,7 +334,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
             float pv = fast_exp2(fmaf(s[qb][r], c, -lv[e]));
-            if (mask && t * BQ + 32 * qb + 8 * rq + 4 * hf + e < kj) pv = 0.f;
+            if (mask) {
+              const int qq = t * BQ + 32 * qb + 8 * rq + 4 * hf + e;
+              if ((CAUSAL && kj > qq + shift) || kj < qq + shift - window) pv = 0.f;
+            }
             s[qb][r] = pv;
             dp[qb][r] = pv * (dp[qb][r] - dd[e]);
           }
@@ -277,14 +356,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
           dk[db] = M::mma(aq, sb[t4], dk[db]);
         }
     }
-    if (t + 1 < n_qt) lstore(buf ^ 1);
+    if (it + 1 < n_it) lstore(buf ^ 1);
     __syncthreads();
   }
 
   // store: lane owns key kj, d rows 32db + 8rq + 4hf + 0..3
-  if (kj < p.s_kv) {
-    T* dkp = (T*)p.dk + bi * p.dk_sb + hi * p.dk_sh + (int64_t)kj * p.dk_ss;
-    T* dvp = (T*)p.dv + bi * p.dv_sb + hi * p.dv_sh + (int64_t)kj * p.dv_ss;
+  if (kj < sq.kv_len) {
+    T* dkp = (T*)p.dk + sq.koff(p.dk_sb, p.dk_sh, p.dk_ss, hk) + (int64_t)kj * p.dk_ss;
+    T* dvp = (T*)p.dv + sq.koff(p.dv_sb, p.dv_sh, p.dv_ss, hk) + (int64_t)kj * p.dv_ss;
     typedef T t4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -303,7 +382,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const float* lse2) {
   constexpr int BK = kDqK, PITCH = D + 8;
   using M = Mfma16<T>;
@@ -317,20 +396,26 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest causal tiles first
   const int bh = blockIdx.x % nbh;
   const int bi = bh / p.h, hi = bh % p.h;
+  const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
+  const Seq<VARLEN> sq(p, bi);
+  if (qt * kDqRows >= sq.q_len) return;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hf = lane / 32, col = lane % 32;
   const int row0 = qt * kDqRows + wave * 32;
   const int qi = row0 + col;
-  const bool q_valid = qi < p.s_q;
+  const bool q_valid = qi < sq.q_len;
+  const int shift = p.bottom_right ? sq.kv_len - sq.q_len : 0;
+  const int window = p.window_left < 0 ? kNoWindow : p.window_left;
 
-  const T* Q = (const T*)p.q + bi * p.q_sb + hi * p.q_sh;
-  const T* G = (const T*)p.dout + bi * p.do_sb + hi * p.do_sh;
-  const T* K = (const T*)p.k + bi * p.k_sb + hi * p.k_sh;
-  const T* V = (const T*)p.v + bi * p.v_sb + hi * p.v_sh;
+  const T* Q = (const T*)p.q + sq.qoff(p.q_sb, p.q_sh, p.q_ss, hi);
+  const T* G = (const T*)p.dout + sq.qoff(p.do_sb, p.do_sh, p.do_ss, hi);
+  const T* K = (const T*)p.k + sq.koff(p.k_sb, p.k_sh, p.k_ss, hk);
+  const T* V = (const T*)p.v + sq.koff(p.v_sb, p.v_sh, p.v_ss, hk);
   const float c = p.scale_log2;
-  const float l2 = q_valid ? lse2[(int64_t)bh * p.s_q + qi] : INFINITY;
-  const float dl = q_valid ? p.delta[(int64_t)bh * p.s_q + qi] : 0.f;
+  const int64_t si = sq.st0(p, hi) + (int64_t)qi * Seq<VARLEN>::st_step(p);
+  const float l2 = q_valid ? lse2[si] : INFINITY;
+  const float dl = q_valid ? p.delta[si] : 0.f;
 
   v8 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -347,32 +432,39 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
-  const int last_q = min(p.s_q, (qt + 1) * kDqRows) - 1;
-  const int kv_end = CAUSAL ? min(p.s_kv, last_q + 1) : p.s_kv;
-  const int n_tiles = (kv_end + BK - 1) / BK;
-  const int wave_kv_end = row0 >= p.s_q ? 0 : (CAUSAL ? min(p.s_kv, min(p.s_q, row0 + 32)) : p.s_kv);
+  // keys of the workgroup's band: [kv_begin, kv_end)
+  const int last_q = min(sq.q_len, (qt + 1) * kDqRows) - 1;
+  const int kv_end = CAUSAL ? min(sq.kv_len, max(last_q + shift + 1, 0)) : sq.kv_len;
+  const int kv_begin = min(kv_end, max(qt * kDqRows + shift - window, 0));
+  const int j0 = kv_begin / BK;
+  const int j1 = kv_end > kv_begin ? (kv_end + BK - 1) / BK : j0;
+  // the wave's band: keys [wave_kv_begin, wave_kv_end)
+  const int w_last = min(sq.q_len, row0 + 32) - 1;
+  const int wave_kv_end =
+      row0 >= sq.q_len ? 0 : (CAUSAL ? min(sq.kv_len, w_last + shift + 1) : sq.kv_len);
+  const int wave_kv_begin = row0 + shift - window;
   LK lk, lv;
   lk.init(tid, p.k_ss, PITCH);
   lv.init(tid, p.v_ss, PITCH);
   i16x8 kr[LK::CPT], vr[LK::CPT];
   auto gload = [&](int j) {
-    lk.load(kr, K + (int64_t)j * BK * p.k_ss, p.s_kv - j * BK);
-    lv.load(vr, V + (int64_t)j * BK * p.v_ss, p.s_kv - j * BK);
+    lk.load(kr, K + (int64_t)j * BK * p.k_ss, sq.kv_len - j * BK);
+    lv.load(vr, V + (int64_t)j * BK * p.v_ss, sq.kv_len - j * BK);
   };
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
-  if (n_tiles > 0) {
-    gload(0);
+  if (j1 > j0) {
+    gload(j0);
     lk.store(kl[0], kr);
     lv.store(vl[0], vr);
   }
   __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+    if (j + 1 < j1) gload(j + 1);
     const int kbase = j * BK;
-    if (kbase < wave_kv_end) {
+    if (kbase < wave_kv_end && kbase + BK > wave_kv_begin) {
       const T* kb_ = kl[buf];
       const T* vb_ = vl[buf];
       f32x16 s[2], dp[2];
@@ -389,7 +481,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
         }
       }
       // lane = query qi; register r of block kb = key kbase + 32kb + 8(r/4) + 4hf + r%4
-      const bool mask = (CAUSAL && kbase + BK - 1 > row0) || kbase + BK > p.s_kv;
+      const bool mask = (CAUSAL && kbase + BK - 1 > row0 + shift) ||
+                        kbase < w_last + shift - window || kbase + BK > sq.kv_len;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -397,7 +490,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
           float pv = fast_exp2(fmaf(s[kb][r], c, -l2));
           if (mask) {
             const int key = kbase + 32 * kb + 8 * (r / 4) + 4 * hf + (r % 4);
-            if ((CAUSAL && key > qi) || key >= p.s_kv) pv = 0.f;
+            if ((CAUSAL && key > qi + shift) || key < qi + shift - window || key >= sq.kv_len)
+              pv = 0.f;
           }
           dp[kb][r] = pv * (dp[kb][r] - dl);
         }
@@ -412,7 +506,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
           dq[db] = M::mma(ak, sb[t4], dq[db]);
         }
     }
-    if (j + 1 < n_tiles) {
+    if (j + 1 < j1) {
       lk.store(kl[buf ^ 1], kr);
       lv.store(vl[buf ^ 1], vr);
     }
@@ -420,7 +514,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
   }
 
   if (q_valid) {
-    T* dqp = (T*)p.dq + bi * p.dq_sb + hi * p.dq_sh + (int64_t)qi * p.dq_ss;
+    T* dqp = (T*)p.dq + sq.qoff(p.dq_sb, p.dq_sh, p.dq_ss, hi) + (int64_t)qi * p.dq_ss;
     typedef T t4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -434,8 +528,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const 
   }
 }
 
-// Fills a (b, h, s, d) tensor with zeros (dK, dV when there are no queries,
-// dQ when there are no keys is covered by the dQ kernel itself).
+// Fills a dense (b, h, s, d) tensor with zeros (dK, dV when there are no
+// queries, dQ when there are no keys).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) zero_rows_kernel(void* x, int64_t sb, int64_t sh,
                                                         int64_t ss, int b, int h, int s) {
@@ -448,60 +542,69 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(void* x, int64_t sb, int
   *(i16x8*)ptr = i16x8{};
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D>
+hipError_t zero_rows(void*& x, int64_t& sb, int64_t& sh, int64_t& ss, int& b, int& h, int& s,
+                     hipStream_t stream) {
+  const long long rows = (long long)b * h * s;
+  const int per = 256 / (D / 8);
+  const dim3 g((unsigned)((rows + per - 1) / per));
+  void* a[] = {&x, &sb, &sh, &ss, &b, &h, &s};
+  return hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a, 0, stream);
+}
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
   BwdParams arg = p;
-  const long long n = (long long)p.b * p.h * p.s_q;
+  const long long n = VARLEN ? (long long)p.total_q * p.h : (long long)p.b * p.h * p.s_q;
   float* lse2 = p.delta + (n + 63) / 64 * 64;
-  const int nbh = p.b * p.h;
   hipError_t e;
-  if (p.s_q == 0 || p.s_kv == 0) {
+  if (!VARLEN && (p.s_q == 0 || p.s_kv == 0)) {
     // nothing to recompute: every gradient is zero
     if (p.s_kv > 0) {
-      const long long rows = (long long)nbh * p.s_kv;
-      const int per = 256 / (D / 8);
-      const dim3 g((unsigned)((rows + per - 1) / per));
-      void* a1[] = {&arg.dk, &arg.dk_sb, &arg.dk_sh, &arg.dk_ss, &arg.b, &arg.h, &arg.s_kv};
-      e = hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a1, 0, stream);
+      e = zero_rows<T, D>(arg.dk, arg.dk_sb, arg.dk_sh, arg.dk_ss, arg.b, arg.h_kv, arg.s_kv,
+                          stream);
       if (e != hipSuccess) return e;
-      void* a2[] = {&arg.dv, &arg.dv_sb, &arg.dv_sh, &arg.dv_ss, &arg.b, &arg.h, &arg.s_kv};
-      return hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a2, 0, stream);
+      return zero_rows<T, D>(arg.dv, arg.dv_sb, arg.dv_sh, arg.dv_ss, arg.b, arg.h_kv, arg.s_kv,
+                             stream);
     }
-    if (p.s_q > 0) {
-      const long long rows = (long long)nbh * p.s_q;
-      const int per = 256 / (D / 8);
-      const dim3 g((unsigned)((rows + per - 1) / per));
-      void* a1[] = {&arg.dq, &arg.dq_sb, &arg.dq_sh, &arg.dq_ss, &arg.b, &arg.h, &arg.s_q};
-      return hipLaunchKernel((const void*)&zero_rows_kernel<T, D>, g, dim3(256), a1, 0, stream);
-    }
+    if (p.s_q > 0)
+      return zero_rows<T, D>(arg.dq, arg.dq_sb, arg.dq_sh, arg.dq_ss, arg.b, arg.h, arg.s_q,
+                             stream);
     return hipSuccess;
   }
-  {
+  if (n > 0) {
     const int rpb = kPreThreads / (D / 8);
-    void* args[] = {&arg, &lse2};
-    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((n + rpb - 1) / rpb)),
-                        dim3(kPreThreads), args, 0, stream);
+    void* args[] = {&arg, &lse2, (void*)&n};
+    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D, VARLEN>,
+                        dim3((unsigned)((n + rpb - 1) / rpb)), dim3(kPreThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  {
-    const long long g = (long long)nbh * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
+  // packed sequences with no queries (or no keys) still get their dK, dV
+  // (or dQ) rows written as zeros by these two kernels
+  const long long gk = (long long)p.b * p.h_kv * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
+  if (gk > 0) {
     void* args[] = {&arg, &lse2};
-    e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL>, dim3((unsigned)g),
+    e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gk),
                         dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  {
-    const long long g = (long long)nbh * ((p.s_q + kDqRows - 1) / kDqRows);
+  const long long gq = (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
+  if (gq > 0) {
     void* args[] = {&arg, &lse2};
-    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL>, dim3((unsigned)g),
+    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gq),
                         dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
   }
-  return e;
+  return hipSuccess;
 }
 
 template <typename T, int D>
-hipError_t launch_d(const BwdParams& p, bool causal, hipStream_t stream) {
-  return causal ? launch_typed<T, D, true>(p, stream) : launch_typed<T, D, false>(p, stream);
+hipError_t launch_d(const BwdParams& p, bool causal, bool varlen, hipStream_t stream) {
+  if (varlen)
+    return causal ? launch_typed<T, D, true, true>(p, stream)
+                  : launch_typed<T, D, false, true>(p, stream);
+  return causal ? launch_typed<T, D, true, false>(p, stream)
+                : launch_typed<T, D, false, false>(p, stream);
 }
 
 }  // namespace
@@ -512,12 +615,14 @@ size_t bwd_workspace_bytes(long long rows) {
   return ((2 * n * sizeof(float)) + 255) / 256 * 256;
 }
 
-hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, bool varlen,
+                      hipStream_t stream) {
   if (dt == Dt::BF16)
-    return d == 64 ? launch_d<__bf16, 64>(p, causal, stream) : launch_d<__bf16, 128>(p, causal, stream);
+    return d == 64 ? launch_d<__bf16, 64>(p, causal, varlen, stream)
+                   : launch_d<__bf16, 128>(p, causal, varlen, stream);
   if (dt == Dt::F16)
-    return d == 64 ? launch_d<_Float16, 64>(p, causal, stream)
-                   : launch_d<_Float16, 128>(p, causal, stream);
+    return d == 64 ? launch_d<_Float16, 64>(p, causal, varlen, stream)
+                   : launch_d<_Float16, 128>(p, causal, varlen, stream);
   return hipErrorInvalidValue;
 }
 

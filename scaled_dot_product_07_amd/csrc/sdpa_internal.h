@@ -56,9 +56,17 @@ struct BwdParams {
   int64_t dq_sb, dq_sh, dq_ss;
   int64_t dk_sb, dk_sh, dk_ss;
   int64_t dv_sb, dv_sh, dv_ss;
-  int b, h, s_q, s_kv;
-  float scale;       // the signed attention scale
-  float scale_log2;  // scale * log2(e)
+  int b, h, s_q, s_kv;  // packed layout: b = sequences, s_q / s_kv = longest sequence
+  int h_kv;             // key/value heads (h is a multiple)
+  int bottom_right;     // diagonal aligned to the bottom-right corner
+  int window_left;      // -1: no left bound
+  float scale;          // the signed attention scale
+  float scale_log2;     // scale * log2(e)
+  // packed (THD) layout only: sequence starts (b + 1 entries) and totals;
+  // row strides are the *_ss fields, *_sb unused
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  int total_q, total_kv;
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (32 per wave)
@@ -71,9 +79,11 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
                       hipStream_t stream);
 
 // Enqueue the three backward kernels; returns the first failing launch status.
-hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, bool varlen,
+                      hipStream_t stream);
 
-// Bytes of backward workspace for `rows` = b * h * s_q query rows: the fp32
+// Bytes of backward workspace for `rows` = b * h * s_q (dense) or total_q * h
+// (packed) query rows: the fp32
 // row dot products rowsum(dO * O) and the statistic in base 2.
 size_t bwd_workspace_bytes(long long rows);
 

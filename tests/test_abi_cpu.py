@@ -31,7 +31,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
-              "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_version"):
+              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_bwd_workspace_size", "sdpa_last_error",
+              "sdpa_version"):
         assert s in syms
 
 
@@ -197,6 +198,85 @@ def bwd(lib, dt=BF16, lse=ALIGNED, ws=ALIGNED, ws_bytes=1 << 20, d=64, b=1, h=1,
 def test_bwd_validation(lib, kw, status, msg):
     assert bwd(lib, **kw) == status
     assert msg in lib.sdpa_last_error().decode()
+
+
+def bwd_ex(lib, h=2, h_kv=2, causal=1, br=0, window=-1, b=1, sq=8, skv=8, d=64, k=ALIGNED,
+           dk=ALIGNED, ws_bytes=1 << 20, kstride=None):
+    qs = dense_st(b, h, sq, d)
+    ks = kstride or dense_st(b, h_kv, skv, d)
+    P = ALIGNED
+    return lib.sdpa_bwd_ex(P, k, P, P, P, ALIGNED, P, dk, P, ALIGNED, ws_bytes, BF16, b, h, h_kv,
+                           sq, skv, d, qs, ks, ks, qs, qs, qs, ks, ks, 0.1, causal, br, window,
+                           None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(h=4, h_kv=3), INVALID, "multiple of h_kv"),
+    (dict(h_kv=-1), INVALID, "negative h_kv"),
+    (dict(br=1, causal=0), INVALID, "bottom_right needs"),
+    (dict(window=-5), INVALID, "window_left"),
+    (dict(h=8, h_kv=2, k=None), INVALID, "k: NULL"),
+    (dict(h=8, h_kv=2, dk=None), INVALID, "dk: NULL"),
+    (dict(kstride=S4(0, 0, 1 << 24, 1)), UNSUPPORTED, "32-bit tile offsets"),
+    (dict(h=4, sq=100, ws_bytes=4 * 100 * 4), INVALID, "smaller"),
+])
+def test_bwd_ex_validation(lib, kw, status, msg):
+    assert bwd_ex(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(h=8, h_kv=2), dict(br=1), dict(causal=0, br=1, window=3),
+                                dict(window=0)])
+def test_bwd_ex_accepts_valid_options_without_work(lib, kw):
+    assert bwd_ex(lib, b=0, **kw) == OK
+
+
+def bwd_varlen(lib, cu_q=ALIGNED, cu_kv=ALIGNED, n=2, tq=16, tkv=16, maxq=8, maxkv=8, h=2, h_kv=2,
+               d=64, dt=BF16, lse=ALIGNED, ws=ALIGNED, ws_bytes=1 << 20, causal=1, br=0,
+               window=-1, qst=None):
+    qs = qst or S3(h * d, d, 1)
+    ks = S3(h_kv * d, d, 1)
+    P = ALIGNED
+    return lib.sdpa_bwd_varlen(P, P, P, P, P, lse, P, P, P, cu_q, cu_kv, n, tq, tkv, maxq, maxkv,
+                               ws, ws_bytes, dt, h, h_kv, d, qs, ks, ks, qs, qs, qs, ks, ks, 0.1,
+                               causal, br, window, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=FP32), UNSUPPORTED, "fp16 and bf16"),
+    (dict(cu_q=None), INVALID, "cu_seqlens"),
+    (dict(cu_kv=None), INVALID, "cu_seqlens"),
+    (dict(maxq=0), INVALID, "max_seqlen"),
+    (dict(maxkv=0), INVALID, "max_seqlen"),
+    (dict(maxq=17), INVALID, "exceeds the totals"),
+    (dict(maxkv=17), INVALID, "exceeds the totals"),
+    (dict(lse=None), INVALID, "lse"),
+    (dict(lse=ALIGNED + 2), UNSUPPORTED, "4-byte"),
+    (dict(ws=None), INVALID, "workspace"),
+    (dict(ws_bytes=16 * 2 * 4), INVALID, "smaller"),
+    (dict(h=6, h_kv=4), INVALID, "multiple of h_kv"),
+    (dict(br=1, causal=0), INVALID, "bottom_right needs"),
+    (dict(d=96), UNSUPPORTED, "head dim"),
+    (dict(qst=S3(2 * 64, 64, 2)), UNSUPPORTED, "innermost"),
+    (dict(n=-1), INVALID, "negative"),
+])
+def test_bwd_varlen_validation(lib, kw, status, msg):
+    assert bwd_varlen(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+def test_bwd_varlen_without_work_is_ok(lib):
+    assert bwd_varlen(lib, n=0, cu_q=None, cu_kv=None) == OK
+    assert bwd_varlen(lib, tq=0, tkv=0, maxq=0, maxkv=0) == OK
+
+
+def test_bwd_varlen_workspace_uses_token_rows(lib):
+    lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
+    # (1, h, total_q) rows: 2 * 16 rows here; one 256-byte block short is refused
+    need = lib.sdpa_bwd_workspace_size(1, 2, 16, 64, BF16)
+    assert need == lib.sdpa_bwd_workspace_size(2, 1, 16, 64, BF16)
+    assert bwd_varlen(lib, ws_bytes=need - 256) == INVALID
+    assert "smaller" in lib.sdpa_last_error().decode()
 
 
 def test_python_binding_maps_statuses(lib):

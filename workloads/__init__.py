@@ -149,19 +149,22 @@ class VarlenInputs:
 
 
 def varlen_inputs(lens_q, lens_kv, h: int, d: int, dtype: str, seed: int,
-                  poison_tail: bool = True, with_dout: bool = False) -> VarlenInputs:
-    """Packed THD tensors with a NaN-filled capacity tail (when poison_tail)."""
+                  poison_tail: bool = True, with_dout: bool = False,
+                  h_kv: Optional[int] = None) -> VarlenInputs:
+    """Packed THD tensors with a NaN-filled capacity tail (when poison_tail);
+    k and v carry h_kv heads (default h)."""
     dt = DTYPES[dtype]
+    h_kv = h if h_kv is None else h_kv
     lens_q = torch.as_tensor(lens_q, dtype=torch.int64)
     lens_kv = torch.as_tensor(lens_kv, dtype=torch.int64)
     cu_q, cu_kv = cu_seqlens(lens_q), cu_seqlens(lens_kv)
     tq, tkv = int(cu_q[-1]), int(cu_kv[-1])
     g = generator(seed)
     bufs = []
-    for tot in (tq, tkv, tkv) + ((tq,) if with_dout else ()):
+    for tot, nh in ((tq, h), (tkv, h_kv), (tkv, h_kv)) + (((tq, h),) if with_dout else ()):
         cap = capacity(tot) if poison_tail else tot
-        t = torch.full((cap, h, d), float("nan"), dtype=dt)
-        t[:tot] = _draw(g, (tot, h, d), dt)
+        t = torch.full((cap, nh, d), float("nan"), dtype=dt)
+        t[:tot] = _draw(g, (tot, nh, d), dt)
         bufs.append(t)
     return VarlenInputs(bufs[0], bufs[1], bufs[2], cu_q, cu_kv, lens_q, lens_kv, tq, tkv,
                         bufs[3] if with_dout else None)
