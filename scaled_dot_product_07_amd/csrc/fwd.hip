@@ -370,11 +370,15 @@ fwd16_kernel(FwdParams p) {
   const int dchunk = (lane % CH) ^ swz(RIT(0) % 16 + drow);  // RIT(x) mod 16 is the same for all x
   const int kvoff = drow * (int)p.k_ss * (int)sizeof(T) + dchunk * 16;
   const int vvoff = drow * (int)p.v_ss * (int)sizeof(T) + dchunk * 16;
-  // buffer resource of key tile t (zero bytes for tiles outside the keys);
-  // built in scalar code outside the fused blocks
-  auto tile_rsrc = [&](const T* __restrict__ base, int64_t stride, int t) -> i32x4 {
-    const T* tb = base + (int64_t)t * BN * stride;
-    const int rows = t < t0 ? 0 : min(kv_end - t * BN, BN);
+  // buffer resource of key tile t0 + t (zero bytes for tiles outside the
+  // keys); built in scalar code outside the fused blocks. Offsets count from
+  // tile t0 so that the per-step addresses stay simple induction variables.
+  const T* __restrict__ K0 = K + (int64_t)t0 * BN * p.k_ss;
+  const T* __restrict__ V0 = V + (int64_t)t0 * BN * p.v_ss;
+  const int kv_rel = kv_end - t0 * BN;  // keys from tile t0 on
+  // (tb: the tile's first row)
+  auto tile_rsrc_at = [&](const T* __restrict__ tb, int64_t stride, int t) -> i32x4 {
+    const int rows = t < 0 ? 0 : min(kv_rel - t * BN, BN);
     const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
     const unsigned long long a = (unsigned long long)tb;
     return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
@@ -393,9 +397,18 @@ fwd16_kernel(FwdParams p) {
     dma(r2.r[XT(x)], vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T),
         vbuf0 + ((u + NBV) % NBV) * VBUF + XT(x) * TILE + RIT(x) * D);
   };
-  auto rsrc2 = [&](const T* __restrict__ base, int64_t stride, int u) -> Rsrc2 {
-    return Rsrc2{{tile_rsrc(base, stride, t0 + 2 * u), tile_rsrc(base, stride, t0 + 2 * u + 1)}};
+  // the two tiles of step u, from the first row of tile 2u (ub)
+  auto rsrc2_at = [&](const T* __restrict__ ub, int64_t stride, int u) -> Rsrc2 {
+    return Rsrc2{{tile_rsrc_at(ub, stride, 2 * u), tile_rsrc_at(ub + BN * stride, stride, 2 * u + 1)}};
   };
+  auto rsrc2 = [&](const T* __restrict__ base, int64_t stride, int u) -> Rsrc2 {
+    return rsrc2_at(base + (int64_t)u * 2 * BN * stride, stride, u);
+  };
+  // first rows of the tiles the next step's loads fill (K of step s+1+LK,
+  // V of step s-1+LV), advanced by one step pair of rows per step so that the
+  // loop carries plain pointer increments
+  const T* kstep_ptr = K0 + (int64_t)(1 + LK) * 2 * BN * p.k_ss;
+  const T* vstep_ptr = V0 + (int64_t)(LV - 1) * 2 * BN * p.v_ss;
 
   // Softmax state (per lane = per query row; both halves agree):
   //   m_cur  offset (log2 units) of the P that the next block computes; after
@@ -583,8 +596,10 @@ fwd16_kernel(FwdParams p) {
   // computes a value that is never used.
   auto step = [&](int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
                   v8(&p_cur)[4]) {
-    const Rsrc2 rk = rsrc2(K, p.k_ss, s + 1 + LK);
-    const Rsrc2 rv = rsrc2(V, p.v_ss, s - 1 + LV);
+    const Rsrc2 rk = rsrc2_at(kstep_ptr, p.k_ss, s + 1 + LK);
+    const Rsrc2 rv = rsrc2_at(vstep_ptr, p.v_ss, s - 1 + LV);
+    kstep_ptr += 2 * BN * p.k_ss;
+    vstep_ptr += 2 * BN * p.v_ss;
     wait_vm(WaitStep{});
     __builtin_amdgcn_s_barrier();
     bool rescale = false;
@@ -638,11 +653,11 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
     for (int b = -(LK + 1); b < 0; ++b) {
       if (b - 1 + LV >= -1) {
-        const Rsrc2 r2 = rsrc2(V, p.v_ss, b - 1 + LV);
+        const Rsrc2 r2 = rsrc2(V0, p.v_ss, b - 1 + LV);
 #pragma unroll
         for (int x = 0; x < CPT; ++x) vdma(r2, b - 1 + LV, x);
       }
-      const Rsrc2 r2 = rsrc2(K, p.k_ss, b + 1 + LK);
+      const Rsrc2 r2 = rsrc2(K0, p.k_ss, b + 1 + LK);
 #pragma unroll
       for (int x = 0; x < CPT; ++x) kdma(r2, b + 1 + LK, x);
     }
