@@ -9,9 +9,11 @@ pages and the readings taken). This module only marshals numpy float64
 arrays into that library through ctypes and builds it with g++ when it is
 missing.
 
-Parity pins (tests/test_oracle_pins.py) tie every function here to something
+Parity pins (tests/test_oracle_pins*.py) tie every function here to something
 other than itself: torch's CPU attention in float64 (the pages' own check),
-closed forms, invariants, finite differences and a hand-worked golden case.
+closed forms, invariants, finite differences and a hand-worked golden case;
+the FP8 decoder is pinned to torch's float8_e4m3fn conversion and to the
+format's defining values.
 """
 
 from __future__ import annotations
@@ -62,7 +64,8 @@ def _load():
                                       P, P, P, P, I]
         lib.oracle_bwd_varlen_ex.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, D, I, I, I64,
                                              P, P, P, P, P, I]
-        for f in ("oracle_attn_rows", "oracle_attn_rows_ex", "oracle_fwd_ex",
+        lib.oracle_e4m3_decode.argtypes = [P, I64, P]
+        for f in ("oracle_e4m3_decode", "oracle_attn_rows", "oracle_attn_rows_ex", "oracle_fwd_ex",
                   "oracle_fwd_varlen_ex", "oracle_bwd_ex", "oracle_bwd_varlen_ex"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -185,3 +188,43 @@ def bwd_varlen(q, k, v, dout, cu_q, cu_kv, scale: float, causal: bool, threads: 
                                  *_mask(causal, bottom_right, window_left), _ptr(o), _ptr(lse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
     return o, lse, dq, dk, dv
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """FP8 E4M3 codes (uint8, any shape) -> exact float64 values (NaN codes -> NaN)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_decode(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def _fp8_inputs(q8, k8, v8, descale_q, descale_k, descale_v):
+    return (float(descale_q) * e4m3_decode(q8), float(descale_k) * e4m3_decode(k8),
+            float(descale_v) * e4m3_decode(v8))
+
+
+def fwd_fp8(q8, k8, v8, scale: float, causal: bool, threads: int = 0, *, descale_q=1.0,
+            descale_k=1.0, descale_v=1.0, scale_o=1.0, bottom_right: bool = False,
+            window_left: int = -1):
+    """Per-tensor scaled FP8 forward, dense: the attention of the decoded inputs
+    times their descales, its output times scale_o (cudnn-frontend PR #554 merge
+    log, the per-tensor FP8 forward entry). q8 [b,h_q,s_q,d], k8/v8 [b,h_kv,s_kv,d]
+    of e4m3 codes. Returns (o, lse, amax) with amax = max |o| (0 when empty).
+    The method's rounding of P to e4m3 is an implementation step, not part of
+    this definition."""
+    q, k, v = _fp8_inputs(q8, k8, v8, descale_q, descale_k, descale_v)
+    o, lse = fwd(q, k, v, scale, causal, threads, bottom_right=bottom_right,
+                 window_left=window_left)
+    o = o * float(scale_o)
+    return o, lse, float(np.max(np.abs(o))) if o.size else 0.0
+
+
+def fwd_fp8_varlen(q8, k8, v8, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0, *,
+                   descale_q=1.0, descale_k=1.0, descale_v=1.0, scale_o=1.0,
+                   bottom_right: bool = False, window_left: int = -1):
+    """Packed THD form of fwd_fp8: q8 [T_q,h_q,d], k8/v8 [T_kv,h_kv,d] e4m3 codes."""
+    q, k, v = _fp8_inputs(q8, k8, v8, descale_q, descale_k, descale_v)
+    o, lse = fwd_varlen(q, k, v, cu_q, cu_kv, scale, causal, threads,
+                        bottom_right=bottom_right, window_left=window_left)
+    o = o * float(scale_o)
+    return o, lse, float(np.max(np.abs(o))) if o.size else 0.0

@@ -32,6 +32,9 @@
 //    output comes from an all-zero P; a zero-length sequence contributes
 //    nothing.
 //
+//  * The same merge log, the per-tensor FP8 forward entry: e4m3 inputs with
+//    per-tensor descales; oracle_e4m3_decode gives their exact values (the
+//    bit layout is the public OCP FP8 one, stated at the function).
 //  * The same pull request's sdpa API: is_causal (top-left), causal_bottom_right
 //    (the diagonal aligned to the bottom-right corner, allowed only with an
 //    active band) and window_left (-1 = unbounded), and grouped-query
@@ -324,6 +327,29 @@ void oracle_bwd_varlen(const double* q, const double* k, const double* v, const 
                        double* dk, double* dv, int threads) {
   oracle_bwd_varlen_ex(q, k, v, dout, cu_q, cu_kv, n_seqs, h, h, d, scale, causal, 0, -1, o, lse,
                        dq, dk, dv, threads);
+}
+
+// FP8 E4M3 codes to doubles, exactly. The pages name the format (the
+// per-tensor FP8 forward of cudnn-frontend PR #554's merge log runs on
+// E4M3/E5M2 inputs) but not its bits; the encoding is the public OCP 8-bit
+// floating point one, in the variant without infinities that the e4m3
+// tensors of torch and the gfx950 conversions use: sign bit 7, exponent
+// bits 6..3 with bias 7, mantissa bits 2..0; exponent field 0 holds the
+// subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is NaN (so the largest
+// finite value is 1.75 * 2^8 = 448).
+void oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const int c = codes[i];
+    const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double x;
+    if (e == 15 && m == 7)
+      x = std::nan("");
+    else if (e == 0)
+      x = std::ldexp((double)m, -9);  // (m / 8) * 2^-6
+    else
+      x = std::ldexp((double)(8 + m), e - 10);  // (1 + m / 8) * 2^(e - 7)
+    out[i] = sign ? -x : x;
+  }
 }
 
 }  // extern "C"
