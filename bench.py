@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0  # dense e4m3 MFMA peak of MI355X
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16s1024d64_causal_counters.json")
 FWD_SOURCE = os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", "fwd.hip")
@@ -299,6 +300,17 @@ def bench_other_workloads(torch, sdpa, W, dev):
     e = _entry(ms, vflops)
     e["total_tokens"] = inp.total_q
     out["fwd_varlen_bf16_32seq_h16d128_causal"] = e
+    # the two dense forward shapes with e4m3 inputs (the workloads' values
+    # rounded to e4m3), bf16 output; priced against the fp8 MFMA peak
+    for c, layout in ((W.FWD_BF16_B4H16S1024D64, "causal"), (W.FWD_BF16_B2H16S4096D128, "bshd")):
+        q, k, v = (x.to(dev).to(torch.float8_e4m3fn) for x in W.case_inputs(c))
+        o = torch.empty(q.shape, device=dev, dtype=torch.bfloat16)
+        ms = time_launches(lambda: sdpa.fwd_fp8(q, k, v, scale=c.scale, causal=c.causal, out=o,
+                                                return_lse=False), 50, 5, torch)
+        e = _entry(ms, fwd_flops(c.b, c.h, c.s_q, c.s_kv, c.d, c.causal))
+        e["frac_of_fp8_mfma_peak"] = round(e["tflops"] / PEAK_FP8_TFLOPS, 4)
+        out[f"fwd_fp8_b{c.b}h{c.h}s{c.s_q}d{c.d}_{layout}"] = e
+        del q, k, v, o
     # causal bf16 backward b4 h16 s2048 d128
     c = W.BWD_BF16_B4H16S2048D128
     q, k, v, do = (x.to(dev) for x in W.case_inputs(c))

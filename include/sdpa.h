@@ -60,7 +60,9 @@ typedef enum {
   SDPA_ERR_LAUNCH = 3
 } sdpa_status;
 
-typedef enum { SDPA_FP32 = 0, SDPA_FP16 = 1, SDPA_BF16 = 2 } sdpa_dtype;
+/* SDPA_FP8_E4M3 (OCP FP8 E4M3, one byte per element) is accepted only by
+ * the sdpa_fwd_fp8* entry points, as their input type. */
+typedef enum { SDPA_FP32 = 0, SDPA_FP16 = 1, SDPA_BF16 = 2, SDPA_FP8_E4M3 = 3 } sdpa_dtype;
 
 /*
  * Dense forward.
@@ -140,6 +142,51 @@ sdpa_status sdpa_fwd_varlen_ex(const void* q, const void* k, const void* v, void
                                const int64_t q_stride[3], const int64_t k_stride[3],
                                const int64_t v_stride[3], const int64_t o_stride[3], float scale,
                                int causal, int bottom_right, int window_left, void* stream);
+
+/*
+ * FP8 forward, dense: Q, K, V hold e4m3 codes (OCP FP8 E4M3, strides in
+ * bytes-as-elements, rows 16-byte aligned), O is written in o_dtype
+ * (SDPA_BF16 or SDPA_FP16).
+ *   descale_q, descale_k, descale_v, scale_o: DEVICE pointers to one fp32
+ *     each, read by the kernel (NULL means 1): the attention runs on
+ *     descale_q * Q, descale_k * K, descale_v * V and stores scale_o * O.
+ *   amax_o: DEVICE pointer to one fp32 or NULL: set to max |stored O| over
+ *     every row, before the cast to o_dtype (the library clears it first).
+ *   lse: as in sdpa_fwd, the statistic of the real scores
+ *     scale * descale_q * descale_k * Q K^T.
+ *   Grouped-query heads and the mask options as in sdpa_fwd_ex.
+ * P (the softmax numerator, at most 2^8 of the row's running offset) is
+ * rounded to e4m3 before the P.V product and l sums the rounded values, so
+ * O differs from the exact result by the rounding of P (relative step 2^-3
+ * per element); the scores are exact products accumulated in fp32.
+ * Cited: cudnn-frontend PR #554, its merge log's per-tensor FP8 d512 forward
+ * entry (descales read on the device, descale_q * descale_k folded into the
+ * log2 softmax scale, descale_v * scale_o into the output factor, Amax_O of
+ * the fp32 output before the cast) and its FP8 forward casting P before the
+ * second product.
+ */
+sdpa_status sdpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const float* descale_q, const float* descale_k, const float* descale_v,
+                         const float* scale_o, float* amax_o, sdpa_dtype o_dtype, int b, int h,
+                         int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                         const int64_t k_stride[4], const int64_t v_stride[4],
+                         const int64_t o_stride[4], float scale, int causal, int bottom_right,
+                         int window_left, void* stream);
+
+/*
+ * FP8 forward, packed THD (as sdpa_fwd_varlen_ex, with the fp8 arguments of
+ * sdpa_fwd_fp8): q (total_q, h, d), k, v (total_kv, h_kv, d) e4m3 codes.
+ */
+sdpa_status sdpa_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const float* descale_q, const float* descale_k,
+                                const float* descale_v, const float* scale_o, float* amax_o,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                                int max_seqlen_kv, sdpa_dtype o_dtype, int h, int h_kv, int d,
+                                const int64_t q_stride[3], const int64_t k_stride[3],
+                                const int64_t v_stride[3], const int64_t o_stride[3],
+                                float scale, int causal, int bottom_right, int window_left,
+                                void* stream);
 
 /*
  * Bytes of device workspace the backward needs for these sizes: two fp32

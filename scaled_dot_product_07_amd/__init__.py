@@ -16,6 +16,9 @@ Entry points (same names as the C ABI, minus the ``sdpa_`` prefix; the
   bwd(q, k, v, o, dout, lse, ...)         dense backward, returns (dq, dk, dv)
   bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_kv, ...)
                                           packed THD backward, returns (dq, dk, dv)
+  fwd_fp8(q, k, v, ...), fwd_fp8_varlen(q, k, v, cu_q, cu_kv, ...)
+                                          e4m3 inputs with per-tensor descales,
+                                          bf16/fp16 output, returns (o, lse)
 Options: grouped-query heads (k, v with fewer heads than q), causal,
 bottom_right (diagonal aligned to the bottom-right corner), window_left.
 """
@@ -29,7 +32,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "bwd", "bwd_varlen", "bwd_workspace_size", "last_error", "version",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_fp8_varlen", "bwd", "bwd_varlen",
+           "bwd_workspace_size", "last_error", "version",
            "library_path", "SdpaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +41,7 @@ _LIB_PATH = os.path.join(_HERE, "libsdpa07.so")
 
 SDPA_OK, SDPA_ERR_INVALID_ARG, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH = 0, 1, 2, 3
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_FP8 = torch.float8_e4m3fn
 
 _lib = None
 
@@ -68,6 +73,10 @@ def _load():
                                     S3, S3, S3, S3, F, I, P]
     lib.sdpa_fwd_varlen_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
                                        S3, S3, S3, S3, F, I, I, I, P]
+    lib.sdpa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                 S4, S4, S4, S4, F, I, I, I, P]
+    lib.sdpa_fwd_fp8_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                        I, I, S3, S3, S3, S3, F, I, I, I, P]
     lib.sdpa_bwd_workspace_size.argtypes = [I, I, I, I, I]
     lib.sdpa_bwd_workspace_size.restype = Z
     lib.sdpa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I,
@@ -77,7 +86,7 @@ def _load():
     lib.sdpa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, Z, I, I,
                                     I, I, S3, S3, S3, S3, S3, S3, S3, S3, F, I, I, I, P]
     for f in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
-              "sdpa_bwd_ex", "sdpa_bwd_varlen"):
+              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_fwd_fp8", "sdpa_fwd_fp8_varlen"):
         getattr(lib, f).restype = I
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.restype = ctypes.c_char_p
@@ -309,3 +318,111 @@ def bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q: torch.Tensor, cu_seqlens_kv:
                              int(bool(bottom_right)), int(window_left), _stream(stream))
     _check(st)
     return dq, dk, dv
+
+
+def _scalar_ptr(t, name):
+    """A one-element fp32 device tensor (or None) as a pointer."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError(f"{name} must be a one-element float32 tensor")
+    return _ptr(t)
+
+
+def _fp8_common(q, k, v, out_dtype, descale_q, descale_k, descale_v, scale_o, amax_o):
+    for t in (q, k, v):
+        if t.dtype != _FP8:
+            raise ValueError("fp8 path expects torch.float8_e4m3fn q, k, v")
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise NotImplementedError("fp8 forward writes bfloat16 or float16 output")
+    return [_scalar_ptr(descale_q, "descale_q"), _scalar_ptr(descale_k, "descale_k"),
+            _scalar_ptr(descale_v, "descale_v"), _scalar_ptr(scale_o, "scale_o"),
+            _scalar_ptr(amax_o, "amax_o")]
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+            causal: bool = False, bottom_right: bool = False, window_left: int = -1,
+            descale_q=None, descale_k=None, descale_v=None, scale_o=None, amax_o=None,
+            out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Dense FP8 forward: q, k, v float8_e4m3fn of logical shape (b, h, s, d).
+
+    descale_* / scale_o: one-element float32 device tensors (None = 1), read by
+    the kernel; amax_o: a one-element float32 device tensor that receives
+    max |o| before the cast. Returns (o, lse) with o in out_dtype.
+    """
+    lib = _load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("dense path expects 4-D (b, h, s, d) tensors")
+    b, h, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    extras = _fp8_common(q, k, v, out_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype)
+    if out.dtype != out_dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape and out_dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, s_q), device=q.device, dtype=torch.float32)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (b, h, s_q)):
+        raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.sdpa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *extras,
+                          _DTYPE_CODE[out_dtype], b, h, h_kv, s_q, s_kv, d, _strides(q, 4),
+                          _strides(k, 4), _strides(v, 4), _strides(out, 4), scale,
+                          int(bool(causal)), int(bool(bottom_right)), int(window_left),
+                          _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def fwd_fp8_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                   cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int, *,
+                   total_q: Optional[int] = None, total_kv: Optional[int] = None,
+                   scale: Optional[float] = None, causal: bool = False,
+                   bottom_right: bool = False, window_left: int = -1, descale_q=None,
+                   descale_k=None, descale_v=None, scale_o=None, amax_o=None,
+                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Packed THD FP8 forward: q (T_q, h, d), k/v (T_kv, h_kv, d) float8_e4m3fn, int32
+    cu_seqlens on the device; the fp8 arguments as in fwd_fp8. Returns (o, lse) with lse
+    (T_q, h) token-major."""
+    lib = _load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed path expects (T, h, d) tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_kv.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.shape != cu_seqlens_kv.shape or cu_seqlens_q.dim() != 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must be 1-D of the same length")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_kv.is_contiguous()):
+        raise ValueError("cu_seqlens must be contiguous")
+    t_q, h, d = q.shape
+    t_kv, h_kv = k.shape[0], k.shape[1]
+    if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k, v")
+    extras = _fp8_common(q, k, v, out_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)
+    total_q = t_q if total_q is None else int(total_q)
+    total_kv = t_kv if total_kv is None else int(total_kv)
+    if total_q > t_q or total_kv > t_kv:
+        raise ValueError("total_q/total_kv exceed the tensors' first dimension")
+    n = cu_seqlens_q.shape[0] - 1
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype)
+    if out.dtype != out_dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape and out_dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((t_q, h), device=q.device, dtype=torch.float32)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.shape[1:] != (h,) or lse.shape[0] < total_q):
+        raise ValueError("lse must be a contiguous float32 (T_q, h) tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.sdpa_fwd_fp8_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *extras,
+                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), n, total_q, total_kv,
+                                 int(max_seqlen_q), int(max_seqlen_kv), _DTYPE_CODE[out_dtype],
+                                 h, h_kv, d, _strides(q, 3), _strides(k, 3), _strides(v, 3),
+                                 _strides(out, 3), scale, int(bool(causal)),
+                                 int(bool(bottom_right)), int(window_left), _stream(stream))
+    _check(st)
+    return out, lse

@@ -26,7 +26,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["abi.cpp", "fwd.hip", "bwd.hip"]
+SOURCES = ["abi.cpp", "fwd.hip", "fwd_fp8.hip", "bwd.hip"]
 
 
 def _compile(src: str, extra) -> str:

@@ -40,7 +40,7 @@ sdpa_status ok() {
   return SDPA_OK;
 }
 
-int elem_size(sdpa_dtype dt) { return dt == SDPA_FP32 ? 4 : 2; }
+int elem_size(sdpa_dtype dt) { return dt == SDPA_FP32 ? 4 : dt == SDPA_FP8_E4M3 ? 1 : 2; }
 
 bool valid_dtype(sdpa_dtype dt) { return dt == SDPA_FP32 || dt == SDPA_FP16 || dt == SDPA_BF16; }
 
@@ -137,6 +137,20 @@ sdpa_status check_workspace(const void* workspace, size_t workspace_bytes, long 
   if (workspace_bytes < need)
     return fail(SDPA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
                 workspace_bytes, need);
+  return SDPA_OK;
+}
+
+// Arguments only the fp8 entry points take.
+sdpa_status check_fp8_extras(sdpa_dtype o_dtype, const float* descale_q, const float* descale_k,
+                             const float* descale_v, const float* scale_o, const float* amax_o) {
+  if (o_dtype != SDPA_BF16 && o_dtype != SDPA_FP16)
+    return fail(SDPA_ERR_UNSUPPORTED, "fp8 forward writes bf16 or fp16 output, not dtype %d",
+                (int)o_dtype);
+  const float* ptrs[5] = {descale_q, descale_k, descale_v, scale_o, amax_o};
+  const char* names[5] = {"descale_q", "descale_k", "descale_v", "scale_o", "amax_o"};
+  for (int i = 0; i < 5; ++i)
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 4 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "%s: pointer is not 4-byte aligned", names[i]);
   return SDPA_OK;
 }
 
@@ -459,6 +473,126 @@ sdpa_status sdpa_bwd_varlen(const void* q, const void* k, const void* v, const v
   return launch_status(
       sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, true, (hipStream_t)stream),
       "sdpa_bwd_varlen");
+}
+
+sdpa_status sdpa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const float* descale_q, const float* descale_k, const float* descale_v,
+                         const float* scale_o, float* amax_o, sdpa_dtype o_dtype, int b, int h,
+                         int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                         const int64_t k_stride[4], const int64_t v_stride[4],
+                         const int64_t o_stride[4], float scale, int causal, int bottom_right,
+                         int window_left, void* stream) {
+  sdpa_status st;
+  if ((st = check_fp8_extras(o_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)) != SDPA_OK)
+    return st;
+  if (b < 0 || h < 0 || s_q < 0 || s_kv < 0 || d < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "negative size");
+  if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
+  if ((st = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st;
+  if ((st = check_heads(h, h_kv)) != SDPA_OK) return st;
+  const bool work = b > 0 && h > 0 && s_q > 0;
+  const int qs[4] = {b, h, s_q, d}, ks[4] = {b, h_kv, s_kv, d};
+  if ((st = check_tensor("q", q, q_stride, qs, 4, SDPA_FP8_E4M3, work)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, qs, 4, o_dtype, work)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, ks, 4, SDPA_FP8_E4M3, work && s_kv > 0)) != SDPA_OK)
+    return st;
+  if ((st = check_tensor("v", v, v_stride, ks, 4, SDPA_FP8_E4M3, work && s_kv > 0)) != SDPA_OK)
+    return st;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
+  const long long n_qtiles = (s_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
+  if ((long long)b * h * n_qtiles > 0x7fffffffLL)
+    return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
+  if (!work) return ok();
+
+  sdpa07::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_ss = q_stride[2];
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_ss = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_ss = v_stride[2];
+  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_ss = o_stride[2];
+  p.b = b; p.h = h; p.h_kv = h_kv; p.s_q = s_q; p.s_kv = s_kv;
+  p.bottom_right = bottom_right; p.window_left = window_left;
+  p.n_qtiles = (int)n_qtiles;
+  p.scale = scale;
+  p.descale_q = descale_q; p.descale_k = descale_k; p.descale_v = descale_v;
+  p.scale_o = scale_o; p.amax_o = amax_o;
+  if (log_enabled())
+    fprintf(stderr,
+            "[sdpa07] fwd_fp8 out=%d b=%d h=%d h_kv=%d s_q=%d s_kv=%d d=%d causal=%d br=%d "
+            "window=%d\n",
+            (int)o_dtype, b, h, h_kv, s_q, s_kv, d, causal, bottom_right, window_left);
+  return launch_status(sdpa07::launch_fwd_fp8(p, to_dt(o_dtype), d, causal != 0, false,
+                                              (hipStream_t)stream),
+                       "sdpa_fwd_fp8");
+}
+
+sdpa_status sdpa_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const float* descale_q, const float* descale_k,
+                                const float* descale_v, const float* scale_o, float* amax_o,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                int num_seqs, int total_q, int total_kv, int max_seqlen_q,
+                                int max_seqlen_kv, sdpa_dtype o_dtype, int h, int h_kv, int d,
+                                const int64_t q_stride[3], const int64_t k_stride[3],
+                                const int64_t v_stride[3], const int64_t o_stride[3],
+                                float scale, int causal, int bottom_right, int window_left,
+                                void* stream) {
+  sdpa_status st;
+  if ((st = check_fp8_extras(o_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)) != SDPA_OK)
+    return st;
+  if (num_seqs < 0 || total_q < 0 || total_kv < 0 || h < 0 || d < 0 || max_seqlen_q < 0 ||
+      max_seqlen_kv < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "negative size");
+  if (d != 64 && d != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID_ARG, "scale is not finite");
+  if ((st = check_mask(causal, bottom_right, window_left)) != SDPA_OK) return st;
+  if ((st = check_heads(h, h_kv)) != SDPA_OK) return st;
+  const bool work = num_seqs > 0 && h > 0 && total_q > 0;
+  if (work && (!cu_seqlens_q || !cu_seqlens_kv))
+    return fail(SDPA_ERR_INVALID_ARG, "packed path needs cu_seqlens_q and cu_seqlens_kv");
+  if (work && (max_seqlen_q <= 0 || max_seqlen_kv <= 0))
+    return fail(SDPA_ERR_INVALID_ARG, "packed path needs max_seqlen_q > 0 and max_seqlen_kv > 0");
+  if (work && max_seqlen_q > total_q)
+    return fail(SDPA_ERR_INVALID_ARG, "max_seqlen_q %d exceeds total_q %d", max_seqlen_q,
+                total_q);
+  const int qs[3] = {total_q, h, d}, ks[3] = {total_kv, h_kv, d};
+  if ((st = check_tensor("q", q, q_stride, qs, 3, SDPA_FP8_E4M3, work)) != SDPA_OK) return st;
+  if ((st = check_tensor("o", o, o_stride, qs, 3, o_dtype, work)) != SDPA_OK) return st;
+  if ((st = check_tensor("k", k, k_stride, ks, 3, SDPA_FP8_E4M3, work && total_kv > 0)) != SDPA_OK)
+    return st;
+  if ((st = check_tensor("v", v, v_stride, ks, 3, SDPA_FP8_E4M3, work && total_kv > 0)) != SDPA_OK)
+    return st;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
+  const long long n_qtiles = (max_seqlen_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
+  if ((long long)num_seqs * h * n_qtiles > 0x7fffffffLL)
+    return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
+  if (!work) return ok();
+
+  sdpa07::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_ss = q_stride[0]; p.q_sh = q_stride[1];
+  p.k_ss = k_stride[0]; p.k_sh = k_stride[1];
+  p.v_ss = v_stride[0]; p.v_sh = v_stride[1];
+  p.o_ss = o_stride[0]; p.o_sh = o_stride[1];
+  p.b = num_seqs; p.h = h; p.h_kv = h_kv;
+  p.bottom_right = bottom_right; p.window_left = window_left;
+  p.n_qtiles = (int)n_qtiles;
+  p.cu_q = cu_seqlens_q; p.cu_kv = cu_seqlens_kv;
+  p.total_q = total_q; p.total_kv = total_kv;
+  p.scale = scale;
+  p.descale_q = descale_q; p.descale_k = descale_k; p.descale_v = descale_v;
+  p.scale_o = scale_o; p.amax_o = amax_o;
+  if (log_enabled())
+    fprintf(stderr,
+            "[sdpa07] fwd_fp8_varlen out=%d n=%d h=%d h_kv=%d T_q=%d T_kv=%d max_q=%d d=%d "
+            "causal=%d br=%d window=%d\n",
+            (int)o_dtype, num_seqs, h, h_kv, total_q, total_kv, max_seqlen_q, d, causal,
+            bottom_right, window_left);
+  return launch_status(sdpa07::launch_fwd_fp8(p, to_dt(o_dtype), d, causal != 0, true,
+                                              (hipStream_t)stream),
+                       "sdpa_fwd_fp8_varlen");
 }
 
 }  // extern "C"

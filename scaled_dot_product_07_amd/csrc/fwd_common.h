@@ -1,0 +1,114 @@
+// Forward helpers shared by the fp16/bf16/fp32 kernels (fwd.hip) and the
+// fp8 kernel (fwd_fp8.hip): work-unit decoding, the band mask on the S^T
+// accumulator layout and the per-tile online softmax.
+#pragma once
+
+#include "kernel_common.h"
+#include "sdpa_internal.h"
+
+namespace sdpa07 {
+namespace {
+
+// Decoded work unit of one workgroup.
+struct Unit {
+  int qt;          // query tile
+  int hi;          // head
+  int q_len, kv_len;
+  int64_t q_off, k_off, v_off, o_off;  // element offsets of row 0 of this (b|seq, h)
+  int64_t lse_off, lse_st;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
+  Unit w;
+  const int nbh = p.b * p.h;
+  const int u = blockIdx.x;
+  w.qt = p.n_qtiles - 1 - u / nbh;  // heaviest causal tiles first
+  const int bh = u % nbh;
+  const int bi = bh / p.h;
+  w.hi = bh % p.h;
+  if constexpr (VARLEN) {
+    const int q0 = min(max(p.cu_q[bi], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[bi + 1], 0), p.total_q);
+    const int k0 = min(max(p.cu_kv[bi], 0), p.total_kv);
+    const int k1 = min(max(p.cu_kv[bi + 1], 0), p.total_kv);
+    w.q_len = max(q1 - q0, 0);
+    w.kv_len = max(k1 - k0, 0);
+    w.q_off = (int64_t)q0 * p.q_ss + (int64_t)w.hi * p.q_sh;
+    w.o_off = (int64_t)q0 * p.o_ss + (int64_t)w.hi * p.o_sh;
+    w.k_off = (int64_t)k0 * p.k_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)k0 * p.v_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
+    w.lse_off = (int64_t)q0 * p.h + w.hi;
+    w.lse_st = p.h;
+  } else {
+    w.q_len = p.s_q;
+    w.kv_len = p.s_kv;
+    w.q_off = (int64_t)bi * p.q_sb + (int64_t)w.hi * p.q_sh;
+    w.o_off = (int64_t)bi * p.o_sb + (int64_t)w.hi * p.o_sh;
+    w.k_off = (int64_t)bi * p.k_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)bi * p.v_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
+    w.lse_off = ((int64_t)bi * p.h + w.hi) * p.s_q;
+    w.lse_st = 1;
+  }
+  return w;
+}
+
+// Per-lane softmax state update for one tile of 32 scores held in s[2][16]
+// (already masked with -inf). Returns alpha, the factor for the old O.
+__device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], float c, float& m_run,
+                                              float& l_run) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  mx = fmaxf(mx, other_half(mx));
+  const float m_new = fmaxf(m_run, mx * c);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  float rs = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = fast_exp2(fmaf(s[mb][r], c, -m_use));
+      s[mb][r] = pv;
+      rs += pv;
+    }
+  l_run = l_run * alpha + rs;
+  m_run = m_new;
+  return alpha;
+}
+
+// Key index held by register r of block mb of S^T in a lane of half hf.
+__device__ __forceinline__ int s_key(int mb, int r, int hf) {
+  return 32 * mb + 8 * (r / 4) + 4 * hf + (r % 4);
+}
+
+// Masks every score of a tile (a neutralised softmax).
+__device__ __forceinline__ void mask_all(f32x16 (&s)[2]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mb][r] = -INFINITY;
+}
+
+// Hides the scores of keys outside the band of each row of a tile: key >
+// qi + shift (causal), key < qi + shift - window, key >= kv_len. shift = 0
+// (top-left) or kv_len - q_len (bottom-right); window is a huge value when
+// there is no left bound.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len, int hf,
+                                          int shift, int window) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kbase + s_key(mb, r, hf);
+      if ((CAUSAL && key > qi + shift) || key < qi + shift - window || key >= kv_len)
+        s[mb][r] = -INFINITY;
+    }
+}
+
+}  // namespace
+}  // namespace sdpa07

@@ -34,6 +34,17 @@ struct FwdParams {
   const int32_t* cu_q;
   const int32_t* cu_kv;
   int total_q, total_kv;
+  // fp8 (e4m3) inputs only: per-tensor factors read on the device (null
+  // means 1): real Q = descale_q * Q, likewise K and V; O is stored as
+  // scale_o * O. amax_o (may be null) receives max |stored O| before the
+  // output cast. scale is the signed attention scale (the kernel folds it
+  // with the descales into its log2 factor).
+  const float* descale_q;
+  const float* descale_k;
+  const float* descale_v;
+  const float* scale_o;
+  float* amax_o;
+  float scale;
 };
 
 // Backward launch parameters (dense).
@@ -77,6 +88,10 @@ constexpr int kFwdThreads16 = 512;  // fp16/bf16 forward workgroup (two key grou
 // Enqueue the forward; returns the launch status.
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
                       hipStream_t stream);
+
+// Enqueue the fp8 (e4m3) forward; `out` is the output dtype (F16 or BF16).
+hipError_t launch_fwd_fp8(const FwdParams& p, Dt out, int d, bool causal, bool varlen,
+                          hipStream_t stream);
 
 // Enqueue the three backward kernels; returns the first failing launch status.
 hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, bool varlen,

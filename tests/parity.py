@@ -6,6 +6,18 @@ Tolerances (written here once, used by every GPU test):
   dQ, dK, dV : max|G - G_ref| <= 5e-2 * max|G_ref| per tensor, with an absolute
                floor of 1e-5 for references that are identically zero (one visible
                key: dS = dP - D vanishes exactly, the GPU leaves ~1e-7 of rounding)
+FP8 forward (e4m3 Q, K, V; P rounded to e4m3 before P.V; O in bf16/fp16):
+  every P value is within a relative 2^-4 of its exact value (round to
+  nearest with 3 mantissa bits; the largest P of a row lies in [2^4, 2^8], so
+  values down to 2^-10 of it are in the normal range; smaller ones round with
+  an absolute step of 2^-10 of the row max), and l sums those rounded values, so
+  LSE : |LSE - LSE_ref| <= -ln(1 - 2^-4) < 0.065, -inf exactly where the oracle has -inf
+  O   : a weighted mean with each weight off by at most that factor; no sharp
+        elementwise bound exists, so the test takes max|O - O_ref| <= 2^-3 max|O_ref|
+        and rms(O - O_ref) <= 2^-5 rms(O_ref) (a wrong index or operand gives errors
+        of the order of O itself); rows whose P is exact (one visible key, or V
+        constant over the keys) are checked to the output rounding in their own tests
+  amax: |amax - amax_ref| <= 2^-3 amax_ref
 The reference is always the fp64 oracle run on the very same input bytes.
 """
 
@@ -21,6 +33,9 @@ O_ABS_TOL_FP32 = 1e-4
 LSE_ABS_TOL = 5e-3
 GRAD_REL_TOL = 5e-2
 GRAD_ABS_FLOOR = 1e-5
+FP8_LSE_ABS_TOL = 0.065
+FP8_O_MAX_REL = 2.0 ** -3
+FP8_O_RMS_REL = 2.0 ** -5
 
 DT_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
 
@@ -64,4 +79,28 @@ def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, what: str) -> float:
     err = float(np.max(np.abs(g_gpu - g_ref))) if g_ref.size else 0.0
     tol = max(GRAD_REL_TOL * ref_max, GRAD_ABS_FLOOR)
     assert err <= tol, f"{what}: max|diff| {err:.3e} > tol {tol:.3e}"
+    return err
+
+
+def check_o_fp8(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "O") -> float:
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
+    if not o_ref.size:
+        return 0.0
+    diff = o_gpu - o_ref
+    err = float(np.max(np.abs(diff)))
+    tol = FP8_O_MAX_REL * float(np.max(np.abs(o_ref)))
+    assert err <= tol, f"{what}: max|diff| {err:.3e} > tol {tol:.3e} (fp8)"
+    rms, rms_ref = float(np.sqrt(np.mean(diff ** 2))), float(np.sqrt(np.mean(o_ref ** 2)))
+    assert rms <= FP8_O_RMS_REL * rms_ref, f"{what}: rms diff {rms:.3e} > {FP8_O_RMS_REL} x {rms_ref:.3e}"
+    return err
+
+
+def check_lse_fp8(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str = "LSE") -> float:
+    dead = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_gpu), dead), f"{what}: -inf pattern differs"
+    live = ~dead
+    if not live.any():
+        return 0.0
+    err = float(np.max(np.abs(lse_gpu[live] - lse_ref[live])))
+    assert err <= FP8_LSE_ABS_TOL, f"{what}: max|diff| {err:.3e} > {FP8_LSE_ABS_TOL} (fp8)"
     return err

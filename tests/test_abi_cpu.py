@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sdpa.h")
 
 OK, INVALID, UNSUPPORTED = 0, 1, 2
-FP32, FP16, BF16 = 0, 1, 2
+FP32, FP16, BF16, FP8 = 0, 1, 2, 3
 ALIGNED = 0x10000  # a fake 16-byte aligned device address: never dereferenced
 
 
@@ -31,8 +31,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
-              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_bwd_workspace_size", "sdpa_last_error",
-              "sdpa_version"):
+              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_fwd_fp8", "sdpa_fwd_fp8_varlen",
+              "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_version"):
         assert s in syms
 
 
@@ -277,6 +277,54 @@ def test_bwd_varlen_workspace_uses_token_rows(lib):
     assert need == lib.sdpa_bwd_workspace_size(2, 1, 16, 64, BF16)
     assert bwd_varlen(lib, ws_bytes=need - 256) == INVALID
     assert "smaller" in lib.sdpa_last_error().decode()
+
+
+def fwd_fp8(lib, out=BF16, h=2, h_kv=2, b=1, sq=8, skv=8, d=64, dq=None, amax=None, qst=None,
+            causal=1, br=0, window=-1, q=ALIGNED):
+    qs = qst or dense_st(b, h, sq, d)
+    ks = dense_st(b, h_kv, skv, d)
+    return lib.sdpa_fwd_fp8(q, ALIGNED, ALIGNED, ALIGNED, None, dq, None, None, None, amax, out,
+                            b, h, h_kv, sq, skv, d, qs, ks, ks, dense_st(b, h, sq, d), 0.1,
+                            causal, br, window, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(out=FP32), UNSUPPORTED, "bf16 or fp16 output"),
+    (dict(out=FP8), UNSUPPORTED, "bf16 or fp16 output"),
+    (dict(dq=ALIGNED + 2), UNSUPPORTED, "descale_q"),
+    (dict(amax=ALIGNED + 1), UNSUPPORTED, "amax_o"),
+    (dict(qst=S4(0, 0, 72, 1)), UNSUPPORTED, "16-byte"),
+    (dict(h=4, h_kv=3), INVALID, "multiple of h_kv"),
+    (dict(br=1, causal=0), INVALID, "bottom_right needs"),
+    (dict(d=256), UNSUPPORTED, "head dim"),
+    (dict(q=None), INVALID, "q: NULL"),
+])
+def test_fwd_fp8_validation(lib, kw, status, msg):
+    assert fwd_fp8(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+def test_fwd_fp8_accepts_byte_strides_without_work(lib):
+    # e4m3 rows of 64 bytes satisfy the 16-byte rule that would refuse 64
+    # bf16 elements at a stride of 72; zero queries launch nothing
+    assert fwd_fp8(lib, sq=0, q=None, h=8, h_kv=2) == OK
+    assert fwd_fp8(lib, sq=0, q=None, out=FP16, qst=S4(0, 0, 80, 1)) == OK
+
+
+def test_fwd_fp8_varlen_validation(lib):
+    s = S3(2 * 64, 64, 1)
+    st = lib.sdpa_fwd_fp8_varlen(ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, None, None, None, None,
+                                 None, None, ALIGNED, 2, 16, 16, 8, 8, BF16, 2, 2, 64, s, s, s, s,
+                                 0.1, 1, 0, -1, None)
+    assert st == INVALID and "cu_seqlens" in lib.sdpa_last_error().decode()
+    st = lib.sdpa_fwd_fp8_varlen(ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, None, None, None, None,
+                                 None, ALIGNED, ALIGNED, 2, 16, 16, 17, 8, BF16, 2, 2, 64, s, s, s,
+                                 s, 0.1, 1, 0, -1, None)
+    assert st == INVALID and "exceeds total_q" in lib.sdpa_last_error().decode()
+    st = lib.sdpa_fwd_fp8_varlen(ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, None, None, None, None,
+                                 None, None, None, 0, 0, 0, 0, 0, BF16, 2, 2, 64, s, s, s, s, 0.1, 1,
+                                 0, -1, None)
+    assert st == OK
 
 
 def test_python_binding_maps_statuses(lib):
