@@ -86,20 +86,24 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsign
 // ---------------------------------------------------------------------------
 // fp16 / bf16 io.
 //
-// A workgroup of 8 waves owns one 128-row query tile of one (b|sequence, h).
-// Waves w and w+4 sit on the same SIMD and own the same 32 query rows; they
-// split the keys: key tile t belongs to wave group t % 2. Both waves of a SIMD
-// therefore get the same work (a causal tile's keys are split evenly), each
-// hides the other's waits, and one barrier serves two key tiles. At the end
-// the two partial results of a row group, (O, offset, l), are merged through
-// LDS. Query tiles are ordered heaviest first so that the hardware's dynamic
-// dispatch of workgroups to CUs balances the causal work (longest first).
+// A workgroup of 8 waves owns two 128-row query tiles A and B of one
+// (b|sequence, h): waves 0-3 hold the rows of A, waves 4-7 those of B, 32
+// rows each, so every SIMD hosts one wave of each tile. Causal attention
+// without a left bound pairs tiles (n-1-i, i): both start at key 0, so one
+// stream of key tiles serves both, and every pair holds the same causal work
+// (the wave of the short tile finishes early and leaves its SIMD to the
+// other, which then runs alone at nearly the same speed per tile). Other
+// masks pair adjacent tiles (2i, 2i+1), whose key ranges nearly coincide.
 //
-// Step s of the key loop is one barrier and one straight-line block per wave
-// (see `block`): the QK^T products of the wave's tile of step s+1, the P.V
-// products of its tile of step s-1 and the softmax of its tile of step s,
-// with the workgroup's share of the LDS stores of K(s+2) and V(s) and of the
-// global loads of later tiles spread over the block.
+// Step s of the key loop loads one 64-key tile of K and V (each wave loads
+// an eighth of it) and runs one straight-line block per wave whose rows see
+// the tile (see `block`): the QK^T products of tile s+1, the P.V products of
+// tile s-1 and the softmax of tile s, with the wave's share of the loads of
+// later tiles spread over the block. A wave takes part in every step's
+// barrier and loads, but computes only over the steps its own rows reach;
+// when they end it drains its last P.V and stores its rows while the other
+// waves go on. No partial results are merged: each wave sees every key tile
+// of its rows.
 //
 // Softmax offsets are lazy: the offset m of a row (log2 units) is raised
 // only when a tile's max exceeds it by more than kTau, so P <= 2^kTau and the
@@ -123,33 +127,30 @@ fwd16_kernel(FwdParams p) {
   // operand reads (ds_read_b128, 16 rows per phase) and the transposing P.V
   // operand reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes) hit
   // distinct banks; each lane loads the global chunk that its slot holds.
-  // Tiles of step u live in buffer u mod NBK (K) / u mod NBV (V); a step's
+  // Tile of step u lives in buffer u mod NBK (K) / u mod NBV (V); a step's
   // loads run LK (K) and LV (V) steps ahead of the block that reads them.
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CH;         // rows per load instruction
-  constexpr int CPT = 2 * BN / RPI / (NT / 64);  // load instructions per wave per tensor per step
-  static_assert(CPT >= 1 && (2 * BN) % (RPI * (NT / 64)) == 0, "tile/workgroup mismatch");
+  constexpr int CPT = BN / RPI / (NT / 64);  // load instructions per wave per tensor per step
+  static_assert(CPT >= 1 && BN % (RPI * (NT / 64)) == 0, "tile/workgroup mismatch");
   constexpr int NBK = 2, NBV = 2;
   constexpr int LK = NBK - 1, LV = NBV - 1;
   constexpr int TILE = BN * D;         // elements per tile
-  constexpr int KBUF = 2 * TILE, VBUF = 2 * TILE;  // one step: the two key groups' tiles
-  constexpr int LDS_ELEMS = NBK * KBUF + NBV * VBUF;
+  constexpr int QROWS = 32 * D;        // elements of one wave's Q rows
+  constexpr int LDS_ELEMS = NBK * TILE + NBV * TILE + 8 * QROWS;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
-  T* const kbuf0 = lds;                 // [NBK][2][TILE]
-  T* const vbuf0 = lds + NBK * KBUF;    // [NBV][2][TILE]
+  T* const kbuf0 = lds;                          // [NBK][TILE]
+  T* const vbuf0 = lds + NBK * TILE;             // [NBV][TILE]
   // chunk permutation of row r (only r mod 16 matters)
   auto swz = [](int r) -> int {
     return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
   };
 
-  // ---- work unit: causal, a pair of query tiles (n-1-i, i) of one
-  // (b|sequence, h), the heavier first, so that every pair holds the same
-  // causal work; otherwise one query tile (all tiles cost the same)
+  // ---- work unit: two query tiles of one (b|sequence, h)
   const int nbh = p.b * p.h;
   const int pair = (int)(blockIdx.x / nbh);
-  constexpr int PASSES = CAUSAL ? 2 : 1;
   const int bh = blockIdx.x % nbh;
   const int bi = bh / p.h, hi = bh % p.h;
   const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
@@ -190,9 +191,50 @@ fwd16_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid % 64;
   // wave-uniform values live in SGPRs so per-wave control flow stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int g = wave / 4;       // key group: key tiles g, g+2, g+4, ...
-  const int rg = wave % 4;      // row group
   const int hf = lane / 32, col = lane % 32;
+
+  // the two tiles: causal without a left bound pairs (n-1-i, i), others
+  // (2i, 2i+1); a missing tile (odd count) is -1
+  const bool heavy_pair = CAUSAL && p.window_left < 0;
+  const int qt_a = heavy_pair ? p.n_qtiles - 1 - pair : 2 * pair;
+  const int qt_b0 = heavy_pair ? pair : 2 * pair + 1;
+  const int qt_b = (heavy_pair ? qt_b0 < qt_a : qt_b0 < p.n_qtiles) ? qt_b0 : -1;
+  // keys a tile's rows see: [lo, hi) (empty when the tile has no rows)
+  auto tile_keys = [&](int qt, int& lo, int& hi2) {
+    if (qt < 0 || qt * BM >= q_len) {
+      lo = hi2 = 0;
+      return;
+    }
+    const int last = min(q_len, (qt + 1) * BM) - 1;
+    hi2 = CAUSAL ? min(kv_len, max(last + shift + 1, 0)) : kv_len;
+    lo = min(hi2, max(qt * BM + shift - window, 0));
+  };
+  int a_lo, a_hi, b_lo, b_hi;
+  tile_keys(qt_a, a_lo, a_hi);
+  tile_keys(qt_b, b_lo, b_hi);
+  // the workgroup's steps: tiles t0 .. t0 + n_steps - 1, one per step
+  const bool a_any = a_hi > a_lo, b_any = b_hi > b_lo;
+  const int kv_begin = !a_any ? b_lo : !b_any ? a_lo : min(a_lo, b_lo);
+  const int kv_end = !a_any ? b_hi : !b_any ? a_hi : max(a_hi, b_hi);
+  const int t0 = kv_begin / BN;
+  const int n_steps = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
+
+  const int qt = wave < 4 ? qt_a : qt_b;   // this wave's tile
+  const int rg = wave % 4;                  // its row group
+  const int row0 = qt * BM + rg * 32;       // first query row of this wave
+  const int qi = row0 + col;                // this lane's query row
+  const bool wave_active = qt >= 0 && row0 < q_len;
+  const bool q_valid = wave_active && qi < q_len;
+  // this wave's keys [wave_lo, wave_hi) and its steps [ws0, ws1)
+  const int wave_last = min(row0 + 31, q_len - 1);
+  const int wave_hi =
+      !wave_active ? 0 : (CAUSAL ? min(kv_len, max(wave_last + shift + 1, 0)) : kv_len);
+  const int wave_lo = min(wave_hi, max(row0 + shift - window, 0));
+  int ws0 = 0, ws1 = 0;
+  if (wave_hi > wave_lo) {
+    ws0 = wave_lo / BN - t0;
+    ws1 = (wave_hi + BN - 1) / BN - t0;
+  }
 
   // s_waitcnt with only a vmcnt bound (gfx9 encoding: expcnt and lgkmcnt at
   // their maxima)
@@ -201,48 +243,14 @@ fwd16_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
   };
   // Before the barrier of step s this wave's loads of K(s+1) and V(s-1) must
-  // have landed: they were issued in blocks s-LK and s-LV (V first, then K,
-  // in each block), so the loads allowed to be outstanding are those issued
+  // have landed: they were issued in steps s-LK and s-LV (V first, then K,
+  // in each step), so the loads allowed to be outstanding are those issued
   // after the later of the two.
   constexpr int WAITN = CPT * (2 * LK - 2 < 2 * LV - 1 ? 2 * LK - 2 : 2 * LV - 1);
   using WaitStep = std::integral_constant<int, WAITN>;
   // the prologue's loads issued after K(0): K(1 .. LK) and V(-1 .. LV-2)
   using WaitK0 = std::integral_constant<int, CPT * (LK + LV)>;
   using WaitAll = std::integral_constant<int, 0>;
-
-  for (int pass = 0; pass < PASSES; ++pass) {
-  const int qt = !CAUSAL ? pair : pass == 0 ? p.n_qtiles - 1 - pair : pair;
-  if (pass == 1 && qt >= p.n_qtiles - 1 - pair) break;  // odd count: middle tile alone
-  if (qt * BM >= q_len) continue;  // uniform over the workgroup
-  if (pass == 1) {
-    // the first tile's epilogue is done with LDS, and its stores have left
-    // the counter that the load waits below count against
-    wait_vm(WaitAll{});
-    __syncthreads();
-  }
-  const int row0 = qt * BM + rg * 32;  // first query row of this wave
-  const int qi = row0 + col;           // this lane's query row
-  const bool wave_active = row0 < q_len;
-  const bool q_valid = wave_active && qi < q_len;
-  const int last_q = min(q_len, (qt + 1) * BM) - 1;
-  // keys any row of the tile sees: [kv_begin, kv_end); the steps start at
-  // the tile pair holding kv_begin (step s covers tiles t0 + 2s, t0 + 2s + 1)
-  const int kv_end = CAUSAL ? min(kv_len, max(last_q + shift + 1, 0)) : kv_len;
-  const int kv_begin = min(kv_end, max(qt * BM + shift - window, 0));
-  const int t0 = kv_begin / (2 * BN) * 2;
-  const int n_tiles = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
-  const int n_steps = (n_tiles + 1) / 2;  // two key tiles per step
-  // this wave's keys [wave_lo, wave_hi) and the steps in which its own tile
-  // (t0 + 2s + g) meets them: [wave_s0, wave_s1)
-  const int wave_last = min(row0 + 31, q_len - 1);
-  const int wave_hi = !wave_active ? 0 : (CAUSAL ? min(kv_len, max(wave_last + shift + 1, 0)) : kv_len);
-  const int wave_lo = min(wave_hi, max(row0 + shift - window, 0));
-  int wave_s0 = 0, wave_s1 = 0;
-  if (wave_hi > wave_lo) {
-    const int tlo = wave_lo / BN - t0, thi = (wave_hi + BN - 1) / BN - t0;  // tiles [tlo, thi)
-    wave_s0 = tlo > g ? (tlo - g + 1) / 2 : 0;
-    wave_s1 = thi > g ? (thi - g + 1) / 2 : 0;
-  }
 
   v8 qf[D / 16];
   f32x16 acc[D / 32];
@@ -251,32 +259,27 @@ fwd16_kernel(FwdParams p) {
   float l_run = 0.f;
   const float c = p.scale_log2;
 
-  // K/V loads: each step the workgroup loads tiles 2s (group 0) and 2s + 1
-  // (group 1), through a buffer resource rebased per tile whose byte bound
-  // ends with the last key row any query of the tile sees (kv_end): rows past
-  // it read as zeros and are masked anyway (rows are disjoint when the row
-  // stride is at least d, which every dense layout satisfies; with
-  // overlapping rows the extra rows are real, finite keys that the mask
-  // hides), with no per-lane test and no memory touched past the keys; a
-  // tile outside the keys is all zeros.
+  // K/V loads: each step the workgroup loads tile t0 + s through a buffer
+  // resource rebased per tile whose byte bound ends with the last key row
+  // any query of the workgroup sees (kv_end): rows past it read as zeros and
+  // are masked anyway (rows are disjoint when the row stride is at least d,
+  // which every dense layout satisfies; with overlapping rows the extra rows
+  // are real, finite keys that the mask hides), with no per-lane test and no
+  // memory touched past the keys; a tile outside the keys is all zeros.
   // Load instruction x of wave w covers rows RIT(x) .. RIT(x) + RPI - 1 of
-  // tile XT(x) of the step; lane l fills row RIT(x) + l / CH, slot l % CH.
-  // (the 8 waves' rows of one instruction x stay within one tile, so the
-  // tile is a compile-time function of x and the resource index is static)
-  static_assert((8 * RPI) % BN == 0 || BN % (8 * RPI) == 0, "instruction rows straddle tiles");
-  auto XT = [](int x) { return 8 * x * RPI / BN; };
-  auto RIT = [&](int x) { return 8 * x * RPI % BN + wave * RPI; };
+  // the tile; lane l fills row RIT(x) + l / CH, slot l % CH.
+  auto RIT = [&](int x) { return (8 * x + wave) * RPI; };
   const int drow = lane / CH;
   const int dchunk = (lane % CH) ^ swz(RIT(0) % 16 + drow);  // RIT(x) mod 16 is the same for all x
+  static_assert((8 * RPI) % 16 == 0, "load rows change the swizzle phase");
   const int kvoff = drow * (int)p.k_ss * (int)sizeof(T) + dchunk * 16;
   const int vvoff = drow * (int)p.v_ss * (int)sizeof(T) + dchunk * 16;
   // buffer resource of key tile t0 + t (zero bytes for tiles outside the
-  // keys); built in scalar code outside the fused blocks. Offsets count from
-  // tile t0 so that the per-step addresses stay simple induction variables.
+  // keys), from the tile's first row tb; built in scalar code outside the
+  // fused blocks
   const T* __restrict__ K0 = K + (int64_t)t0 * BN * p.k_ss;
   const T* __restrict__ V0 = V + (int64_t)t0 * BN * p.v_ss;
   const int kv_rel = kv_end - t0 * BN;  // keys from tile t0 on
-  // (tb: the tile's first row)
   auto tile_rsrc_at = [&](const T* __restrict__ tb, int64_t stride, int t) -> i32x4 {
     const int rows = t < 0 ? 0 : min(kv_rel - t * BN, BN);
     const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
@@ -287,28 +290,24 @@ fwd16_kernel(FwdParams p) {
     lds_dma16(rs, voff, soff,
               (unsigned)(size_t)(__attribute__((address_space(3))) T*)dst);
   };
-  // the loads of instruction x of step u's K (V) tiles into their buffer
-  // (u >= -1; step -1 is all zeros)
-  auto kdma = [&](const Rsrc2& r2, int u, int x) {
-    dma(r2.r[XT(x)], kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T),
-        kbuf0 + (u % NBK) * KBUF + XT(x) * TILE + RIT(x) * D);
+  // this wave's load instruction x of tile u's K (V) into its buffer (u >= -1;
+  // tile -1 is all zeros)
+  auto kdma = [&](i32x4 r, int u, int x) {
+    dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T),
+        kbuf0 + (u % NBK) * TILE + RIT(x) * D);
   };
-  auto vdma = [&](const Rsrc2& r2, int u, int x) {
-    dma(r2.r[XT(x)], vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T),
-        vbuf0 + ((u + NBV) % NBV) * VBUF + XT(x) * TILE + RIT(x) * D);
+  auto vdma = [&](i32x4 r, int u, int x) {
+    dma(r, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T),
+        vbuf0 + ((u + NBV) % NBV) * TILE + RIT(x) * D);
   };
-  // the two tiles of step u, from the first row of tile 2u (ub)
-  auto rsrc2_at = [&](const T* __restrict__ ub, int64_t stride, int u) -> Rsrc2 {
-    return Rsrc2{{tile_rsrc_at(ub, stride, 2 * u), tile_rsrc_at(ub + BN * stride, stride, 2 * u + 1)}};
-  };
-  auto rsrc2 = [&](const T* __restrict__ base, int64_t stride, int u) -> Rsrc2 {
-    return rsrc2_at(base + (int64_t)u * 2 * BN * stride, stride, u);
+  auto rsrc = [&](const T* __restrict__ base, int64_t stride, int u) -> i32x4 {
+    return tile_rsrc_at(base + (int64_t)u * BN * stride, stride, u);
   };
   // first rows of the tiles the next step's loads fill (K of step s+1+LK,
-  // V of step s-1+LV), advanced by one step pair of rows per step so that the
+  // V of step s-1+LV), advanced by one tile of rows per step so that the
   // loop carries plain pointer increments
-  const T* kstep_ptr = K0 + (int64_t)(1 + LK) * 2 * BN * p.k_ss;
-  const T* vstep_ptr = V0 + (int64_t)(LV - 1) * 2 * BN * p.v_ss;
+  const T* kstep_ptr = K0 + (int64_t)(1 + LK) * BN * p.k_ss;
+  const T* vstep_ptr = V0 + (int64_t)(LV - 1) * BN * p.v_ss;
 
   // Softmax state (per lane = per query row; both halves agree):
   //   m_cur  offset (log2 units) of the P that the next block computes; after
@@ -383,7 +382,7 @@ fwd16_kernel(FwdParams p) {
                                                    ((c ^ sv1) * 8) + vcol % 8));
     return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // S of the first step alone (its P.V and softmax have nothing to do)
+  // S of a wave's first tile alone (its P.V and softmax have nothing to do)
   auto qk_only = [&](const T* kb, f32x16(&s_out)[2]) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
@@ -392,7 +391,7 @@ fwd16_kernel(FwdParams p) {
         s_out[mb] = M::mma(read_k(kb, ks, mb), qf[ks], ks == 0 ? f32x16{} : s_out[mb]);
     mx_nxt = row_max(s_out);
   };
-  // the last P.V alone (after the last step)
+  // a wave's last P.V alone (after its last step)
   auto pv_only = [&](const T* vb, const v8(&p_last)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -400,9 +399,9 @@ fwd16_kernel(FwdParams p) {
       for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
   };
   auto block = [&](int s, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
-                   v8(&p_cur)[4], const Rsrc2& rk, const Rsrc2& rv) {
-    const T* kb = kbuf0 + ((s + 1) % NBK) * KBUF + g * TILE;       // K of step s+1
-    const T* vb = vbuf0 + ((s + NBV - 1) % NBV) * VBUF + g * TILE;  // V of step s-1
+                   v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) {
+    const T* kb = kbuf0 + ((s + 1) % NBK) * TILE;        // K of step s+1
+    const T* vb = vbuf0 + ((s + NBV - 1) % NBV) * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
       if (i < NQK) return read_k(kb, i / 2, i % 2);
       return read_v(vb, (i - NQK) / (D / 32), (i - NQK) % (D / 32));
@@ -485,37 +484,43 @@ fwd16_kernel(FwdParams p) {
     for (int t = 0; t < 4; ++t) p_cur[t] = __builtin_bit_cast(v8, pk[t]);
   };
 
-  // Step s (0 .. n_steps-1): the wait for this wave's loads of the tiles the
-  // block reads, one barrier (every wave's loads have then landed, and every
-  // wave is done with the buffers this block's loads overwrite), the offset
-  // decision for the wave's tile of step s and its block. Every block runs
-  // the same fused code; the edges are neutralised by data instead of
-  // separate code paths: a fully masked S_cur makes the softmax a no-op
-  // (P = 0, so the next block's P.V adds nothing), P_prev = 0 with the zero
-  // tiles of step -1 makes step 0's P.V a no-op, and an unneeded QK only
-  // computes a value that is never used.
-  auto step = [&](int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
-                  v8(&p_cur)[4]) {
-    const Rsrc2 rk = rsrc2_at(kstep_ptr, p.k_ss, s + 1 + LK);
-    const Rsrc2 rv = rsrc2_at(vstep_ptr, p.v_ss, s - 1 + LV);
-    kstep_ptr += 2 * BN * p.k_ss;
-    vstep_ptr += 2 * BN * p.v_ss;
+  // The start of step s, common to every wave: the descriptors of the tiles
+  // this step's loads fill, the wait for this wave's loads of the tiles the
+  // step reads, and one barrier (every wave's loads have then landed, and
+  // every wave is done with the buffers this step's loads overwrite).
+  auto step_begin = [&](int s, i32x4& rk, i32x4& rv) {
+    rk = tile_rsrc_at(kstep_ptr, p.k_ss, s + 1 + LK);
+    rv = tile_rsrc_at(vstep_ptr, p.v_ss, s - 1 + LV);
+    kstep_ptr += BN * p.k_ss;
+    vstep_ptr += BN * p.v_ss;
     wait_vm(WaitStep{});
     __builtin_amdgcn_s_barrier();
-    bool rescale = false;
-    if (s < wave_s0 || s >= wave_s1) {
-      mask_all(s_cur);
-      a_cur = 1.f;
-    } else {
-      const int kbase = (t0 + 2 * s + g) * BN;  // this wave's current key tile
-      float mx = mx_nxt;
-      if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
-          kbase + BN > kv_len) {
-        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window);
-        mx = row_max(s_cur);
-      }
-      rescale = decide(mx);
+  };
+  // A step without a block: the wave's share of the step's loads only.
+  auto light_step = [&](int s) {
+    i32x4 rk, rv;
+    step_begin(s, rk, rv);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) vdma(rv, s - 1 + LV, x);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) kdma(rk, s + 1 + LK, x);
+  };
+  // Step s with a block: the offset decision for the wave's tile of step s,
+  // then the fused block. Every block runs the same code; the first block's
+  // P.V is neutralised by data (P_prev = 0), and the last block's QK of the
+  // next tile computes a value that is never used.
+  auto step = [&](int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
+                  v8(&p_cur)[4]) {
+    i32x4 rk, rv;
+    step_begin(s, rk, rv);
+    const int kbase = (t0 + s) * BN;  // this step's key tile
+    float mx = mx_nxt;
+    if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
+        kbase + BN > kv_len) {
+      mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window);
+      mx = row_max(s_cur);
     }
+    const bool rescale = decide(mx);
     const float a_blk = a_cur;
     block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
     if (rescale) {
@@ -524,160 +529,127 @@ fwd16_kernel(FwdParams p) {
     }
   };
 
-  if (n_steps > 0) {
-    // Prologue: the query tile's 128 rows into LDS with the layout of one
-    // step's two K tiles (rows past the sequence read as zeros), in the V
-    // buffer that no load touches before block 0; then the loads that blocks
-    // -(LK+1) .. -1 would have issued, in the blocks' order (V(b-1+LV) when
-    // it is a step >= -1, then K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2)
-    // (V(-1), read by step 0's no-op P.V, is all zeros). Only Q and K(0)
-    // have to land before the first block; the steps' own waits cover the
-    // rest.
-    T* const qbuf = vbuf0 + (LV - 1) * VBUF;
-    {
-      const int q_rows = q_len - qt * BM;
-      auto q_rsrc = [&](int h) -> i32x4 {
-        const T* qb = Q + (int64_t)(qt * BM + h * BN) * p.q_ss;
-        const int rows = min(q_rows - h * BN, BN);
-        const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T);
-        const unsigned long long a = (unsigned long long)qb;
-        return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
-      };
-      const Rsrc2 rq{{q_rsrc(0), q_rsrc(1)}};
-      const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + dchunk * 16;
+  // Epilogue of a wave: combine the two lane halves' partial sums, normalise
+  // and store its rows (4 consecutive d per lane), and the statistic.
+  auto epilogue = [&]() {
+    const float l_tot = l_run + other_half(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (q_valid) {
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      T* orow = O + (int64_t)qi * p.o_ss;
 #pragma unroll
-      for (int x = 0; x < CPT; ++x)
-        dma(rq.r[XT(x)], qvoff, RIT(x) * (int)p.q_ss * (int)sizeof(T),
-            qbuf + XT(x) * TILE + RIT(x) * D);
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          t4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
+          *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
+        }
+      if (hf == 0 && p.lse)
+        p.lse[lse_off + (int64_t)qi * lse_st] =
+            l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
+  };
+
+  if (n_steps == 0) {
+    epilogue();  // no key anywhere: O = 0, LSE = -inf
+    return;
+  }
+
+  // Prologue: this wave's 32 query rows into its own LDS area (rows past the
+  // sequence read as zeros), then the loads that steps -(LK+1) .. -1 would
+  // have issued, in the steps' order (V(b-1+LV) when it is a step >= -1, then
+  // K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2) (V(-1), read by a first block's
+  // no-op P.V, is all zeros). Only Q and K(0) have to land before the first
+  // block; the steps' own waits cover the rest.
+  T* const qbuf = lds + NBK * TILE + NBV * TILE + wave * QROWS;
+  {
+    const int rows = wave_active ? min(q_len - row0, 32) : 0;
+    const T* qb = Q + (int64_t)max(row0, 0) * p.q_ss;
+    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T);
+    const unsigned long long a = (unsigned long long)qb;
+    const i32x4 rq = {(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes,
+                      kBufferFlags};
+    // instruction x fills rows x * RPI + lane / CH of the wave's 32, each
+    // lane the global chunk that its slot holds under that row's swizzle
 #pragma unroll
-    for (int b = -(LK + 1); b < 0; ++b) {
-      if (b - 1 + LV >= -1) {
-        const Rsrc2 r2 = rsrc2(V0, p.v_ss, b - 1 + LV);
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) vdma(r2, b - 1 + LV, x);
-      }
-      const Rsrc2 r2 = rsrc2(K0, p.k_ss, b + 1 + LK);
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) kdma(r2, b + 1 + LK, x);
+    for (int x = 0; x < 32 / RPI; ++x) {
+      const int qdchunk = (lane % CH) ^ swz((x * RPI + drow) % 16);
+      const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + qdchunk * 16;
+      dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T), qbuf + x * RPI * D);
     }
-    static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
-    f32x16 sa[2], sb[2];
-    v8 pa[4], pb[4];
+  }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pa[t] = v8{};
-      pb[t] = v8{};
-    }
-    wait_vm(WaitK0{});  // this wave's loads of Q and K(0); then every wave's
-    __builtin_amdgcn_s_barrier();
-    // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7]
-    // (read before the barrier of step 0, after which block 0 reloads qbuf)
+  for (int b = -(LK + 1); b < 0; ++b) {
+    if (b - 1 + LV >= -1) {
+      const i32x4 r = rsrc(V0, p.v_ss, b - 1 + LV);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      i16x8 raw = *(const i16x8*)&qbuf[(rg * 32 + col) * D + (((2 * ks + hf) ^ sk) * 8)];
-      if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
-      qf[ks] = __builtin_bit_cast(v8, raw);
+      for (int x = 0; x < CPT; ++x) vdma(r, b - 1 + LV, x);
     }
-    qk_only(kbuf0 + g * TILE, sa);  // S of step 0 (K(0) is in buffer 0)
-    // even steps: S_cur = sa, S_next = sb, P_prev = pb, P_cur = pa; odd
-    // steps the other way round
-    int s = 0;
-    for (; s + 1 < n_steps; s += 2) {
+    const i32x4 r = rsrc(K0, p.k_ss, b + 1 + LK);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) kdma(r, b + 1 + LK, x);
+  }
+  static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
+  f32x16 sa[2], sb[2];
+  v8 pa[4], pb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    pa[t] = v8{};
+    pb[t] = v8{};
+  }
+  wait_vm(WaitK0{});  // this wave's loads of Q and K(0); then every wave's
+  __builtin_amdgcn_s_barrier();
+  // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7]
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    i16x8 raw = *(const i16x8*)&qbuf[col * D + (((2 * ks + hf) ^ sk) * 8)];
+    if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
+    qf[ks] = __builtin_bit_cast(v8, raw);
+  }
+  if (ws1 > ws0 && ws0 == 0) qk_only(kbuf0, sa);  // S of step 0 (K(0) is in buffer 0)
+
+  int s = 0;
+  // steps before this wave's first tile; the last of them computes S of
+  // that tile (K(ws0) has landed at its barrier)
+  for (; s < ws0; ++s) {
+    light_step(s);
+    if (s == ws0 - 1) qk_only(kbuf0 + (ws0 % NBK) * TILE, sa);
+  }
+  // this wave's steps: even offsets from ws0 use S_cur = sa, S_next = sb,
+  // P_prev = pb, P_cur = pa; odd ones the other way round
+  bool last_in_pa = true;
+  if (ws1 > ws0) {
+    for (; s + 1 < ws1; s += 2) {
       step(s, sa, sb, pb, pa);
       step(s + 1, sb, sa, pa, pb);
     }
-    if (s < n_steps) step(s, sa, sb, pb, pa);
-    // the P.V of the wave's tile of the last step, if it had one
-    wait_vm(WaitStep{});
-    __builtin_amdgcn_s_barrier();
-    if (n_steps - 1 >= wave_s0 && n_steps - 1 < wave_s1) {
-      const T* vb = vbuf0 + ((n_steps - 1) % NBV) * VBUF + g * TILE;
-      if ((n_steps - 1) & 1) pv_only(vb, pb);
-      else pv_only(vb, pa);
+    last_in_pa = s < ws1;
+    if (s < ws1) {
+      step(s, sa, sb, pb, pa);
+      ++s;
     }
   }
-
-  // Merge the two key groups of each row group through LDS and store. Wave
-  // w (group g) finalises d-half g of its 32 rows: it publishes the other
-  // half of its O^T with its (offset, l) in slot w, and merges its own half
-  // with the partner's (wave w ^ 4, the other group on the same SIMD). The
-  // K buffers hold the exchange (8 slots of NV floats per lane fill them
-  // exactly), the V buffers the per-wave transposes for the stores.
-  constexpr int NB = D / 64;      // accumulator blocks per d-half
-  constexpr int NV = 16 * NB + 2;  // floats per lane: half of O^T, offset, l
-  static_assert(8 * NV * 64 * 4 <= (int)sizeof(lds), "merge buffer too small");
-  float* xl = reinterpret_cast<float*>(lds);
-  // (the halves are selected with compile-time indices: a runtime index
-  // into acc would move the accumulator to scratch memory)
-  f32x16 mine[NB], other[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    mine[b] = g == 0 ? acc[b] : acc[NB + b];
-    other[b] = g == 0 ? acc[NB + b] : acc[b];
+  // the P.V of the wave's last tile (its V is intact until two steps later),
+  // then its rows leave while the other waves go on
+  auto drain_and_store = [&]() {
+    if (ws1 > ws0) {
+      const T* vb = vbuf0 + ((ws1 - 1) % NBV) * TILE;
+      if (last_in_pa) pv_only(vb, pa);
+      else pv_only(vb, pb);
+    }
+    epilogue();
+  };
+  for (; s < n_steps; ++s) {
+    light_step(s);
+    if (s == ws1 || (ws1 <= ws0 && s == 0)) drain_and_store();
   }
-  // every load of this wave has landed (the last blocks' loads past the keys
-  // still write zeros into their buffers), then every wave's; and every
-  // block has finished with the K/V buffers
+  // the steps' end: every wave's last loads have landed (and the final
+  // barrier keeps the LDS alive for the waves still draining)
   wait_vm(WaitAll{});
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xl[(wave * NV + 16 * b + r) * 64 + lane] = other[b][r];
-  xl[(wave * NV + 16 * NB) * 64 + lane] = m_cur;
-  xl[(wave * NV + 16 * NB + 1) * 64 + lane] = l_run;
-  __syncthreads();
-  const int pw = wave ^ 4;
-  f32x16 oh[NB];  // this wave's d-half of O^T, merged
-  {
-    const float m1 = xl[(pw * NV + 16 * NB) * 64 + lane];
-    const float l1 = xl[(pw * NV + 16 * NB + 1) * 64 + lane];
-    const float m = fmaxf(m_cur, m1);
-    const float mr = m == -INFINITY ? 0.f : m;
-    const float f0 = fast_exp2(m_cur - mr), f1 = fast_exp2(m1 - mr);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        oh[b][r] = mine[b][r] * f0 + xl[(pw * NV + 16 * b + r) * 64 + lane] * f1;
-    l_run = l_run * f0 + l1 * f1;
-    m_cur = m;
-  }
-
-  // Epilogue: combine the two lane halves' partial sums, normalise, and
-  // store through a per-wave LDS transpose so that each lane writes 16
-  // contiguous bytes and a store instruction covers whole row segments.
-  const float l_tot = l_run + other_half(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  constexpr int HD = D / 2;     // d values per half
-  constexpr int TP = HD + 8;    // transpose row pitch (elements)
-  constexpr int XL_ELEMS = 8 * NV * 64 * 4 / (int)sizeof(T);  // the exchange area
-  static_assert(XL_ELEMS + 8 * 32 * TP <= LDS_ELEMS, "transpose buffer too small");
-  T* tl = lds + XL_ELEMS + wave * 32 * TP;
-  typedef T t4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      t4 ov;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = (T)(oh[b][4 * rq + e] * inv);
-      *(t4*)&tl[col * TP + 32 * b + 8 * rq + 4 * hf] = ov;
-    }
-  constexpr int CPR = HD / 8;           // 16-byte chunks per half row
-  constexpr int RPI = 64 / CPR;         // rows per store instruction
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + lane / CPR, cc = lane % CPR;
-    const i16x8 v = *(const i16x8*)&tl[r * TP + 8 * cc];
-    if (row0 + r < q_len)
-      *(i16x8*)(O + (int64_t)(row0 + r) * p.o_ss + g * HD + 8 * cc) = v;
-  }
-  if (g == 0 && hf == 0 && q_valid && p.lse)
-    p.lse[lse_off + (int64_t)qi * lse_st] =
-        l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }  // pass
+  __builtin_amdgcn_s_barrier();
+  if (ws1 == n_steps && ws1 > ws0) drain_and_store();
 }
 
 // ---------------------------------------------------------------------------
@@ -820,8 +792,8 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 const void* pick_kernel(Dt dt) {
-  // fp16/bf16 kernels run 8-wave split-key workgroups; the fp32 kernel runs
-  // 4-wave workgroups.
+  // fp16/bf16 kernels run 8-wave workgroups over two query tiles; the fp32
+  // kernel runs 4-wave workgroups.
   switch (dt) {
     case Dt::BF16: return (const void*)&fwd16_kernel<__bf16, D, CAUSAL, VARLEN>;
     case Dt::F16: return (const void*)&fwd16_kernel<_Float16, D, CAUSAL, VARLEN>;
@@ -843,10 +815,9 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   const void* fn = d == 64 ? pick_kernel<64>(dt, causal, varlen)
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
-  // fp16/bf16: 8-wave split-key workgroups, over causal tile pairs
+  // fp16/bf16: 8-wave workgroups over pairs of query tiles
   const bool paired = dt != Dt::F32;
-  const long long grid =
-      (long long)(paired && causal ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
+  const long long grid = (long long)(paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};
