@@ -515,9 +515,12 @@ fwd16_kernel(FwdParams p) {
     step_begin(s, rk, rv);
     const int kbase = (t0 + s) * BN;  // this step's key tile
     float mx = mx_nxt;
-    if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
-        kbase + BN > kv_len) {
-      mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window);
+    const bool cut_causal = CAUSAL && kbase + BN - 1 > row0 + shift;
+    const bool cut_left = kbase < wave_last + shift - window;
+    const bool cut_end = kbase + BN > kv_len;
+    if (cut_causal || cut_left || cut_end) {
+      mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
+                        cut_end);
       mx = row_max(s_cur);
     }
     const bool rescale = decide(mx);
@@ -750,9 +753,12 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[ks], s[mb], 0, 0, 0);
         }
       }
-      if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
-          kbase + BN > w.kv_len)
-        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf, shift, window);
+      const bool cut_causal = CAUSAL && kbase + BN - 1 > row0 + shift;
+      const bool cut_left = kbase < wave_last + shift - window;
+      const bool cut_end = kbase + BN > w.kv_len;
+      if (cut_causal || cut_left || cut_end)
+        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf, shift, window, cut_causal, cut_left,
+                          cut_end);
       const float alpha = softmax_tile(s, c, m_run, l_run);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;

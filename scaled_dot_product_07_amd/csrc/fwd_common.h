@@ -96,18 +96,39 @@ __device__ __forceinline__ void mask_all(f32x16 (&s)[2]) {
 // Hides the scores of keys outside the band of each row of a tile: key >
 // qi + shift (causal), key < qi + shift - window, key >= kv_len. shift = 0
 // (top-left) or kv_len - q_len (bottom-right); window is a huge value when
-// there is no left bound.
+// there is no left bound. Each bound is applied only when it cuts the tile
+// (the caller's wave-uniform flags), as one compare per score of the key's
+// offset in the tile (a constant per register, plus 4 hf) against a per-lane
+// limit.
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len, int hf,
-                                          int shift, int window) {
+                                          int shift, int window, bool cut_causal, bool cut_left,
+                                          bool cut_end) {
+  const int base = kbase + 4 * hf;  // key of offset s_key(mb, r, 0) is base + that offset
+  if (CAUSAL && cut_causal) {
+    const int lim = qi + shift - base;  // visible iff offset <= lim
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kbase + s_key(mb, r, hf);
-      if ((CAUSAL && key > qi + shift) || key < qi + shift - window || key >= kv_len)
-        s[mb][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r)
+        if (s_key(mb, r, 0) > lim) s[mb][r] = -INFINITY;
+  }
+  if (cut_left) {
+    const int lim = qi + shift - window - base;  // visible iff offset >= lim
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (s_key(mb, r, 0) < lim) s[mb][r] = -INFINITY;
+  }
+  if (cut_end) {
+    const int lim = kv_len - base;  // visible iff offset < lim
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (s_key(mb, r, 0) >= lim) s[mb][r] = -INFINITY;
+  }
 }
 
 }  // namespace

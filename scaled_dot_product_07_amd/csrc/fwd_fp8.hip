@@ -215,9 +215,12 @@ fwd8_kernel(FwdParams p) {
           s[mb] = mfma8(a, qf[kk], s[mb]);
         }
       }
-      if ((CAUSAL && kbase + BN - 1 > row0 + shift) || kbase < wave_last + shift - window ||
-          kbase + BN > w.kv_len)
-        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf, shift, window);
+      const bool cut_causal = CAUSAL && kbase + BN - 1 > row0 + shift;
+      const bool cut_left = kbase < wave_last + shift - window;
+      const bool cut_end = kbase + BN > w.kv_len;
+      if (cut_causal || cut_left || cut_end)
+        mask_tile<CAUSAL>(s, kbase, qi, w.kv_len, hf, shift, window, cut_causal, cut_left,
+                          cut_end);
       // lazy offset: raise it (and rescale O and l) only when the tile's max
       // exceeds it by more than kF8Tau (the rescale factor is the same with
       // or without the lift)

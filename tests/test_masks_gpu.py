@@ -105,8 +105,12 @@ def test_varlen_options_vs_oracle(gpu, h, h_kv, causal, br, window):
 
 
 def test_option_defaults_match_plain_forward(gpu):
-    """h_kv == h, top-left, no window: bit-identical to the plain forward's
-    outputs on the headline-shaped workload's first head group."""
+    """Options that change nothing on the headline-shaped workload: bottom-right
+    alignment with s_q == s_kv takes the same path (bit-identical); a window
+    wider than the keys is the same attention computed with another work
+    split (a left-bounded band pairs adjacent query tiles instead of splitting
+    the heavy tile of a causal pair), so it agrees to the rounding of the
+    output and of the fp32 partial sums."""
     import scaled_dot_product_07_amd as sdpa
     announce("fwd options defaults")
     c = W.FWD_BF16_B4H16S1024D64
@@ -115,5 +119,7 @@ def test_option_defaults_match_plain_forward(gpu):
     b2 = sdpa.fwd(q, k, v, scale=c.scale, causal=True, bottom_right=True)  # s_q == s_kv
     b3 = sdpa.fwd(q, k, v, scale=c.scale, causal=True, window_left=4096)   # wider than the keys
     torch.cuda.synchronize()
-    for other in (b2, b3):
-        assert torch.equal(a[0], other[0]) and torch.equal(a[1], other[1])
+    assert torch.equal(a[0], b2[0]) and torch.equal(a[1], b2[1])
+    d_o = (a[0].float() - b3[0].float()).abs()
+    assert float(d_o.max()) <= 2.0 ** -7 * float(a[0].float().abs().max())
+    assert float((a[1] - b3[1]).abs().max()) <= 1e-3
