@@ -99,7 +99,8 @@ __device__ __forceinline__ void mask_all(f32x16 (&s)[2]) {
 // there is no left bound. Each bound is applied only when it cuts the tile
 // (the caller's wave-uniform flags), as one compare per score of the key's
 // offset in the tile (a constant per register, plus 4 hf) against a per-lane
-// limit.
+// limit and a select (a conditional store instead became a chain of
+// exec-mask updates).
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int kv_len, int hf,
                                           int shift, int window, bool cut_causal, bool cut_left,
@@ -110,24 +111,21 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kbase, int qi, int
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (s_key(mb, r, 0) > lim) s[mb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) s[mb][r] = s_key(mb, r, 0) > lim ? -INFINITY : s[mb][r];
   }
   if (cut_left) {
     const int lim = qi + shift - window - base;  // visible iff offset >= lim
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (s_key(mb, r, 0) < lim) s[mb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) s[mb][r] = s_key(mb, r, 0) < lim ? -INFINITY : s[mb][r];
   }
   if (cut_end) {
     const int lim = kv_len - base;  // visible iff offset < lim
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (s_key(mb, r, 0) >= lim) s[mb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) s[mb][r] = s_key(mb, r, 0) >= lim ? -INFINITY : s[mb][r];
   }
 }
 
