@@ -44,7 +44,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0  # dense e4m3 MFMA peak of MI355X
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16s1024d64_causal_counters.json")
-FWD_SOURCE = os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", "fwd.hip")
+FWD_SOURCES = [os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", f)
+               for f in ("fwd.hip", "fwd_common.h", "kernel_common.h")]
 
 
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
@@ -83,7 +84,7 @@ def summarize_counters(fetch_dir, write_dir):
     out = {
         "kernel": "fwd16_kernel<bf16, d64, causal, dense>",
         "workload": "b4 h16 s1024 d64 causal bf16 BHSD",
-        "fwd_source_sha256_16": source_digest(FWD_SOURCE),
+        "fwd_source_sha256_16": source_digest(FWD_SOURCES),
         "fetch_kib_per_dispatch": f_fwd, "write_kib_per_dispatch": w_fwd,
         "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "copy_bytes": COPY_BYTES,
         "fetch_scale": kf, "write_scale": kw,
@@ -103,9 +104,13 @@ def fwd_flops(b, h, s_q, s_kv, d, causal):
     return f * 0.5 if causal else f
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    """First 16 hex digits of the SHA-256 of the forward kernel's sources."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_launches(fn, steps, warmup, torch, graph=True):
@@ -164,7 +169,7 @@ def traffic_from_counters():
             s = json.load(f)
     except (OSError, ValueError):
         return None
-    if s.get("fwd_source_sha256_16") != source_digest(FWD_SOURCE):
+    if s.get("fwd_source_sha256_16") != source_digest(FWD_SOURCES):
         return None
     return s.get("hbm_bytes_per_launch")
 
