@@ -196,8 +196,12 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------------------
+// Two waves per SIMD hide the LDS and MFMA latencies of one wave behind the
+// other; at d = 128 the dK/dV accumulators, K/V operands and scores need more
+// registers than that allows, so that kernel keeps one.
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, const float* lse2) {
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   constexpr int BQ = kDkdvQ, PITCH = D + 8;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
@@ -383,7 +387,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv_kernel(BwdParams p, cons
 
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(BwdParams p, const float* lse2) {
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dq_kernel(BwdParams p, const float* lse2) {
   constexpr int BK = kDqK, PITCH = D + 8;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
