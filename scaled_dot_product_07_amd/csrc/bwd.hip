@@ -49,7 +49,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPreThreads = 256;
 constexpr int kBwdThreads = 256;
-constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave)
+constexpr int kDkdvThreads = 512;  // four wave pairs
+constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave pair)
 constexpr int kDkdvQ = 64;      // queries per streamed tile
 constexpr int kDqRows = 128;    // queries per dQ workgroup (32 per wave)
 constexpr int kDqK = 64;        // keys per streamed tile
@@ -196,20 +197,33 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Two waves per SIMD hide the LDS and MFMA latencies of one wave behind the
-// other; at d = 128 the dK/dV accumulators, K/V operands and scores need more
-// registers than that allows, so that kernel keeps one.
+// dK/dV: a pair of waves owns 32 keys of one K/V head, and the workgroup's
+// four pairs own 128 consecutive keys. The first wave of a pair (K side)
+// keeps the K rows of its keys as MFMA B operands; per query tile it computes
+// S = Q K^T and P, accumulates dV^T += dO^T P and leaves P in LDS (fp32, in
+// the C layout both waves share). Its partner (V side) keeps the V rows and
+// runs one tile behind: it finishes the previous tile's dS = P (dP - D) with
+// the P its partner left there and accumulates dK^T += Q^T dS, then computes
+// this tile's dP = dO V^T. Each wave thus needs half the registers of one
+// that does both sides, so two waves share a SIMD and hide each other's LDS
+// and MFMA latencies; both do 32 MFMAs per tile, and one barrier per tile
+// orders them. 64-query tiles of Q (three buffers, as the V side reads the
+// previous one), dO (two) and their LSE and D of every query head that reads
+// this K/V head stream through LDS, so dK and dV sum over the head group in
+// registers.
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+__global__ void __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   constexpr int BQ = kDkdvQ, PITCH = D + 8;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  using LQ = TileLoader<T, D, BQ, kBwdThreads>;
-  __shared__ __attribute__((aligned(16))) T ql[2][BQ * PITCH];
+  using LQ = TileLoader<T, D, BQ, kDkdvThreads>;
+  __shared__ __attribute__((aligned(16))) T ql[3][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) T gl[2][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) float l2l[2][BQ];
   __shared__ __attribute__((aligned(16))) float dll[2][BQ];
+  // P of each pair and tile parity: [query block][register quad][lane][4]
+  __shared__ __attribute__((aligned(16))) float pl[2][4][2 * 4 * 64 * 4];
 
   const int nbh = p.b * p.h_kv;
   const int kt = blockIdx.x / nbh;  // key tile; the first ones see the most queries
@@ -220,35 +234,30 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   if (kt * kDkdvKeys >= sq.kv_len) return;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int pair = wave % 4;
+  const bool kside = wave < 4;
   const int hf = lane / 32, col = lane % 32;
-  const int key0 = kt * kDkdvKeys + wave * 32;  // first key of this wave
+  const int key0 = kt * kDkdvKeys + pair * 32;  // first key of this pair
   const int kj = key0 + col;                     // this lane's key
   const int shift = p.bottom_right ? sq.kv_len - sq.q_len : 0;
   const int window = p.window_left < 0 ? kNoWindow : p.window_left;
-
-  const T* K = (const T*)p.k + sq.koff(p.k_sb, p.k_sh, p.k_ss, hk);
-  const T* V = (const T*)p.v + sq.koff(p.v_sb, p.v_sh, p.v_ss, hk);
   const float c = p.scale_log2;
   const int st_step = Seq<VARLEN>::st_step(p);
 
-  // this lane's K and V rows as B operands (B[k = d][n = key])
-  v8 kf[D / 16], vf[D / 16];
+  // this lane's K (or V) row as B operands (B[k = d][n = key])
+  const T* R = kside ? (const T*)p.k + sq.koff(p.k_sb, p.k_sh, p.k_ss, hk)
+                     : (const T*)p.v + sq.koff(p.v_sb, p.v_sh, p.v_ss, hk);
+  const int64_t r_ss = kside ? p.k_ss : p.v_ss;
+  v8 bf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    i16x8 a = {}, b = {};
-    if (kj < sq.kv_len) {
-      a = *(const i16x8*)(K + (int64_t)kj * p.k_ss + 16 * ks + 8 * hf);
-      b = *(const i16x8*)(V + (int64_t)kj * p.v_ss + 16 * ks + 8 * hf);
-    }
-    kf[ks] = __builtin_bit_cast(v8, a);
-    vf[ks] = __builtin_bit_cast(v8, b);
+    i16x8 a = {};
+    if (kj < sq.kv_len) a = *(const i16x8*)(R + (int64_t)kj * r_ss + 16 * ks + 8 * hf);
+    bf[ks] = __builtin_bit_cast(v8, a);
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   // Query rows that see a key of this workgroup: i + shift >= first key
   // (causal) and i + shift - window <= last key.
@@ -257,7 +266,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   const int i_hi = min(sq.q_len - 1, key_hi - shift + window);
   const int t_lo = i_lo / BQ;
   const int nt = i_hi >= i_lo ? i_hi / BQ + 1 - t_lo : 0;  // query tiles per head
-  // the tiles this wave's keys reach (inclusive bounds)
+  // the tiles this pair's keys reach (inclusive bounds)
   const int wt_lo = CAUSAL ? max(key0 - shift, 0) / BQ : 0;
   const int wi_hi = min(key0 + 31, sq.kv_len - 1) - shift + window;
   const int wt_hi = key0 < sq.kv_len && wi_hi >= 0 ? wi_hi / BQ : -1;
@@ -284,103 +293,159 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       dlr = qrow < sq.q_len ? p.delta[si] : 0.f;
     }
   };
-  auto lstore = [&](int buf) {
-    lq.store(ql[buf], qr);
-    lg.store(gl[buf], gr);
+  auto lstore = [&](int it, int qslot) {
+    lq.store(ql[qslot], qr);
+    lg.store(gl[it & 1], gr);
     if (tid < BQ) {
-      l2l[buf][tid] = l2r;
-      dll[buf][tid] = dlr;
+      l2l[it & 1][tid] = l2r;
+      dll[it & 1][tid] = dlr;
     }
+  };
+  auto active = [&](int it) {  // the pair's keys see tile it (the same for both waves)
+    const int t = t_lo + it % nt;
+    return t >= wt_lo && t <= wt_hi;
   };
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+  // acc += A2^T X over the 64 queries of a tile, A2^T read through the
+  // transposing LDS read (dO^T for dV, Q^T for dK)
+  auto accumulate = [&](const T* a2, const f32x16 (&x)[2]) {
+    v8 xb[4];
+    pack_b<T>(x, xb);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const v8 a = read_tr<T, PITCH>(a2, 16 * t4 + vrow, 32 * db + vcol);
+        acc[db] = M::mma(a, xb[t4], acc[db]);
+      }
+  };
+  // x = A1 B over the d columns, A1 rows read from LDS (Q for S, dO for dP);
+  // C layout: lane = key kj, register r of block qb = query
+  // t*BQ + 32qb + 8(r/4) + 4hf + r%4
+  auto product = [&](const T* a1, f32x16 (&x)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      x[qb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const v8 a = *(const v8*)&a1[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
+        x[qb] = M::mma(a, bf[ks], x[qb]);
+      }
+    }
+  };
 
   if (n_it > 0) {
     gload(0);
-    lstore(0);
+    lstore(0, 0);
   }
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_it) gload(it + 1);
-    const int t = t_lo + it % nt;
-    if (t >= wt_lo && t <= wt_hi) {
-      const T* qb_ = ql[buf];
-      const T* gb_ = gl[buf];
-      f32x16 s[2], dp[2];
+  // Both loops run n_it + 1 steps with one barrier each; tile it sits in Q
+  // buffer it % 3 (kept as qs) and in the other buffers at parity it & 1.
+  if (kside) {
+    f32x16 x[2];
+    for (int it = 0, qs = 0; it <= n_it; ++it) {
+      const int qn = qs == 2 ? 0 : qs + 1;
+      if (it + 1 < n_it) gload(it + 1);
+      if (it < n_it && active(it)) {
+        product(ql[qs], x);  // S = Q K^T
+        const int q_first = (t_lo + it % nt) * BQ;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const v8 aq = *(const v8*)&qb_[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
-          const v8 ag = *(const v8*)&gb_[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
-          s[qb] = M::mma(aq, kf[ks], s[qb]);
-          dp[qb] = M::mma(ag, vf[ks], dp[qb]);
-        }
-      }
-      // P and dS in the C layout: lane = key kj, register r of block qb =
-      // query t*BQ + 32qb + 8(r/4) + 4hf + r%4. The band cuts this tile if
-      // its first query hides the wave's last key (causal) or its last
-      // query hides the wave's first key (window).
-      const bool mask = (CAUSAL && key0 + 31 > t * BQ + shift) ||
-                        key0 < t * BQ + BQ - 1 + shift - window;
+          for (int rq = 0; rq < 4; ++rq) {
+            const float4 l4 = *(const float4*)&l2l[it & 1][32 * qb + 8 * rq + 4 * hf];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const float4 l4 = *(const float4*)&l2l[buf][32 * qb + 8 * rq + 4 * hf];
-          const float4 d4 = *(const float4*)&dll[buf][32 * qb + 8 * rq + 4 * hf];
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            float pv = fast_exp2(fmaf(s[qb][r], c, -lv[e]));
-            if (mask) {
-              const int qq = t * BQ + 32 * qb + 8 * rq + 4 * hf + e;
-              if ((CAUSAL && kj > qq + shift) || kj < qq + shift - window) pv = 0.f;
-            }
-            s[qb][r] = pv;
-            dp[qb][r] = pv * (dp[qb][r] - dd[e]);
+            for (int e = 0; e < 4; ++e)
+              x[qb][4 * rq + e] = fast_exp2(fmaf(x[qb][4 * rq + e], c, -lv[e]));
           }
-        }
-      v8 pb[4], sb[4];
-      pack_b<T>(s, pb);
-      pack_b<T>(dp, sb);
-      // dV^T += dO^T P, dK^T += Q^T dS (contraction over the 64 queries)
+        // The band cuts the tile at the causal edge if its first query hides
+        // the pair's last key, at the window's edge if its last query hides
+        // the pair's first key. Query 32qb + 8rq + e (+ q_first + 4hf) hides
+        // key kj when causal and kj > query + shift, or kj < query + shift - W.
+        if (CAUSAL && key0 + 31 > q_first + shift) {
+          const int lim = kj - shift - q_first - 4 * hf;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const v8 ag = read_tr<T, PITCH>(gb_, 16 * t4 + vrow, 32 * db + vcol);
-          const v8 aq = read_tr<T, PITCH>(qb_, 16 * t4 + vrow, 32 * db + vcol);
-          dv[db] = M::mma(ag, pb[t4], dv[db]);
-          dk[db] = M::mma(aq, sb[t4], dk[db]);
+            for (int r = 0; r < 16; ++r)
+              x[qb][r] = 32 * qb + 8 * (r / 4) + r % 4 < lim ? 0.f : x[qb][r];
         }
+        if (key0 < q_first + BQ - 1 + shift - window) {
+          const int lim = kj - shift + window - q_first - 4 * hf;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              x[qb][r] = 32 * qb + 8 * (r / 4) + r % 4 > lim ? 0.f : x[qb][r];
+        }
+        float* pp = pl[it & 1][pair];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *(float4*)&pp[((qb * 4 + rq) * 64 + lane) * 4] =
+                float4{x[qb][4 * rq], x[qb][4 * rq + 1], x[qb][4 * rq + 2], x[qb][4 * rq + 3]};
+        accumulate(gl[it & 1], x);  // dV^T += dO^T P
+      }
+      if (it + 1 < n_it) lstore(it + 1, qn);
+      __syncthreads();
+      qs = qn;
     }
-    if (it + 1 < n_it) lstore(buf ^ 1);
-    __syncthreads();
+  } else {
+    f32x16 x[2];  // dP - D of the previous tile
+    for (int it = 0, qs = 0, qp = 2; it <= n_it; ++it) {
+      const int qn = qs == 2 ? 0 : qs + 1;
+      if (it + 1 < n_it) gload(it + 1);
+      if (it > 0 && active(it - 1)) {
+        // dS = P (dP - D) of the previous tile, then dK^T += Q^T dS
+        const float* pp = pl[(it - 1) & 1][pair];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const float4 p4 = *(const float4*)&pp[((qb * 4 + rq) * 64 + lane) * 4];
+            x[qb][4 * rq] = p4.x * x[qb][4 * rq];
+            x[qb][4 * rq + 1] = p4.y * x[qb][4 * rq + 1];
+            x[qb][4 * rq + 2] = p4.z * x[qb][4 * rq + 2];
+            x[qb][4 * rq + 3] = p4.w * x[qb][4 * rq + 3];
+          }
+        accumulate(ql[qp], x);
+      }
+      if (it < n_it && active(it)) {
+        product(gl[it & 1], x);  // dP = dO V^T
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const float4 d4 = *(const float4*)&dll[it & 1][32 * qb + 8 * rq + 4 * hf];
+            const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[qb][4 * rq + e] -= dd[e];
+          }
+      }
+      if (it + 1 < n_it) lstore(it + 1, qn);
+      __syncthreads();
+      qp = qs;
+      qs = qn;
+    }
   }
 
   // store: lane owns key kj, d rows 32db + 8rq + 4hf + 0..3
   if (kj < sq.kv_len) {
-    T* dkp = (T*)p.dk + sq.koff(p.dk_sb, p.dk_sh, p.dk_ss, hk) + (int64_t)kj * p.dk_ss;
-    T* dvp = (T*)p.dv + sq.koff(p.dv_sb, p.dv_sh, p.dv_ss, hk) + (int64_t)kj * p.dv_ss;
+    T* dst = kside ? (T*)p.dv + sq.koff(p.dv_sb, p.dv_sh, p.dv_ss, hk) + (int64_t)kj * p.dv_ss
+                   : (T*)p.dk + sq.koff(p.dk_sb, p.dk_sh, p.dk_ss, hk) + (int64_t)kj * p.dk_ss;
+    const float f = kside ? 1.f : p.scale;
     typedef T t4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        t4v a, b;
+        t4v a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (T)(dk[db][4 * rq + e] * p.scale);
-          b[e] = (T)dv[db][4 * rq + e];
-        }
-        *(t4v*)(dkp + 32 * db + 8 * rq + 4 * hf) = a;
-        *(t4v*)(dvp + 32 * db + 8 * rq + 4 * hf) = b;
+        for (int e = 0; e < 4; ++e) a[e] = (T)(acc[db][4 * rq + e] * f);
+        *(t4v*)(dst + 32 * db + 8 * rq + 4 * hf) = a;
       }
   }
 }
@@ -590,7 +655,7 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
   if (gk > 0) {
     void* args[] = {&arg, &lse2};
     e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gk),
-                        dim3(kBwdThreads), args, 0, stream);
+                        dim3(kDkdvThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   const long long gq = (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
