@@ -165,6 +165,22 @@ __device__ __forceinline__ void pack_b(const f32x16 (&x)[2], typename Mfma16<T>:
   }
 }
 
+// The same for one 32-key block: 16 values into the 2 B operands of a
+// 32-deep contraction (element e of MFMA t: register 8t + e).
+template <typename T>
+__device__ __forceinline__ void pack_b1(const f32x16& x, typename Mfma16<T>::v8 (&out)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    i32x4 pk;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const f32x2 v = {x[8 * t + 2 * e2], x[8 * t + 2 * e2 + 1]};
+      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
+    }
+    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
+  }
+}
+
 // Loads one tile of `ROWS` rows x D of a (rows, d) tensor whose row r is at
 // base + r * stride, rows at or past `rows` reading as zeros.
 template <typename T, int D, int ROWS, int NT>
@@ -339,6 +355,11 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
     gload(0);
     lstore(0, 0);
   }
+  // Every load issued so far (the B-operand rows above all) has landed on
+  // every path into the loop; without this the compiler cannot tell, and
+  // waits for all outstanding loads, the next tile's included, at their
+  // first use in each iteration.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // Both loops run n_it + 1 steps with one barrier each; tile it sits in Q
   // buffer it % 3 (kept as qs) and in the other buffers at parity it & 1.
@@ -529,6 +550,7 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
     lk.store(kl[0], kr);
     lv.store(vl[0], vr);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // as in the dK/dV kernel: the Q, dO rows have landed
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
     const int buf = (j - j0) & 1;
@@ -537,44 +559,57 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
     if (kbase < wave_kv_end && kbase + BK > wave_kv_begin) {
       const T* kb_ = kl[buf];
       const T* vb_ = vl[buf];
-      f32x16 s[2], dp[2];
+      // The band cuts the tile at the causal edge if the wave's first query
+      // hides the tile's last key, at the window's edge if its last query
+      // hides the tile's first key, and at the end of the keys.
+      const bool cut_causal = CAUSAL && kbase + BK - 1 > row0 + shift;
+      const bool cut_left = kbase < w_last + shift - window;
+      const bool cut_end = kbase + BK > sq.kv_len;
+      // The tile's two 32-key blocks one after the other (fewer live
+      // registers): S^T = K Q^T and dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+      // Lane = query qi; register r of block kb = key
+      // kbase + 32kb + 8(r/4) + 4hf + r%4.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+        f32x16 sv = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const v8 ak = *(const v8*)&kb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
           const v8 av = *(const v8*)&vb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
-          s[kb] = M::mma(ak, qf[ks], s[kb]);
-          dp[kb] = M::mma(av, gf[ks], dp[kb]);
+          sv = M::mma(ak, qf[ks], sv);
+          dp = M::mma(av, gf[ks], dp);
         }
-      }
-      // lane = query qi; register r of block kb = key kbase + 32kb + 8(r/4) + 4hf + r%4
-      const bool mask = (CAUSAL && kbase + BK - 1 > row0 + shift) ||
-                        kbase < w_last + shift - window || kbase + BK > sq.kv_len;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], c, -l2));
+        // key offset 32kb + 8(r/4) + r%4 (+ kbase + 4hf) against each bound
+        const int base = kbase + 32 * kb + 4 * hf;
+        if (CAUSAL && cut_causal) {
+          const int lim = qi + shift - base;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(fmaf(s[kb][r], c, -l2));
-          if (mask) {
-            const int key = kbase + 32 * kb + 8 * (r / 4) + 4 * hf + (r % 4);
-            if ((CAUSAL && key > qi + shift) || key < qi + shift - window || key >= sq.kv_len)
-              pv = 0.f;
+          for (int r = 0; r < 16; ++r) sv[r] = 8 * (r / 4) + r % 4 > lim ? 0.f : sv[r];
+        }
+        if (cut_left) {
+          const int lim = qi + shift - window - base;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = 8 * (r / 4) + r % 4 < lim ? 0.f : sv[r];
+        }
+        if (cut_end) {
+          const int lim = sq.kv_len - base;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = 8 * (r / 4) + r % 4 >= lim ? 0.f : sv[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = sv[r] * (dp[r] - dl);
+        v8 sb[2];
+        pack_b1<T>(dp, sb);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const v8 ak = read_tr<T, PITCH>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol);
+            dq[db] = M::mma(ak, sb[t], dq[db]);
           }
-          dp[kb][r] = pv * (dp[kb][r] - dl);
-        }
-      v8 sb[4];
-      pack_b<T>(dp, sb);
-      // dQ^T += K^T dS^T (contraction over the 64 keys)
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const v8 ak = read_tr<T, PITCH>(kb_, 16 * t4 + vrow, 32 * db + vcol);
-          dq[db] = M::mma(ak, sb[t4], dq[db]);
-        }
+      }
     }
     if (j + 1 < j1) {
       lk.store(kl[buf ^ 1], kr);
