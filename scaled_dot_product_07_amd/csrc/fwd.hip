@@ -105,14 +105,28 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsign
 // waves go on. No partial results are merged: each wave sees every key tile
 // of its rows.
 //
-// Softmax offsets are lazy: the offset m of a row (log2 units) is raised
-// only when a tile's max exceeds it by more than kTau, so P <= 2^kTau and the
-// O accumulator is rescaled only on those (rare) tiles; the result is exact
-// either way because O and l always share the same offset. The decision is
-// taken between blocks, from the row max that the previous block computed.
+// Softmax offsets are lazy: the offset m of a row (log2 units) changes only
+// when a tile's scores rise well above it, and O and l always share it, so
+// the result is exact whichever offsets are taken. Two ways of choosing it:
+//  * checked after the fact (d = 64, where the softmax is the larger share
+//    of a block's work): a block computes the P of its tile with the current
+//    offset and the sum r of the rounded P over the lane's 32 scores, but no
+//    row max. Right after the block, when every lane has r <= kSumMax (so
+//    every P <= kSumMax, far inside the range of the 16-bit P) the sum joins
+//    l; otherwise (scores well above the offset, an overflowed P, or a row
+//    with no offset yet) the tile's scores, still in registers, give the new
+//    offset m' = max(m, c * rowmax), O and l are rescaled by 2^(m - m') and
+//    the tile's P is recomputed before the next block multiplies it into O.
+//    A wave's first tile sets the offset from its own row max.
+//  * decided before the block (d = 128, where the scores cannot stay live
+//    through the block within the register budget): the previous block also
+//    computes the row max of the next tile's scores, and the offset is raised
+//    to it only when it exceeds the offset by more than kTau, so P <= 2^kTau;
+//    the O rescale then runs after that block.
 // The scale stays in fp32 (P = 2^(c*S - m), one fma per score): folding it
 // into Q would round c*Q to the io type and shift scores by up to 2^-9 of
 // their size.
+constexpr float kSumMax = 4096.f;
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
@@ -310,12 +324,16 @@ fwd16_kernel(FwdParams p) {
   const T* vstep_ptr = V0 + (int64_t)(LV - 1) * BN * p.v_ss;
 
   // Softmax state (per lane = per query row; both halves agree):
-  //   m_cur  offset (log2 units) of the P that the next block computes; after
-  //          that block, also the offset of l and of O
-  //   a_cur  factor for l (in the block) and for O (after it) when the
-  //          offset was raised before the block, else 1
-  //   mx_nxt row max of the raw scores S the last block produced
+  //   m_cur  offset (log2 units) of l, of O and of the P that the next block
+  //          computes (-inf while the row has seen no score); with decided
+  //          offsets l and O take it only once that block has run
+  //   a_cur  (decided offsets) factor for l (in the block) and for O (after
+  //          it) when the offset was raised before the block, else 1
+  //   mx_nxt (decided offsets) row max of the raw scores the last block
+  //          produced
+  constexpr bool CHECK_AFTER = D <= 64;
   float m_cur = -INFINITY, a_cur = 1.f, mx_nxt = -INFINITY;
+  constexpr int NPAIR = 16;  // 32 scores per lane, in pairs
   auto row_max = [&](const f32x16(&sv)[2]) -> float {
     float a = fmaxf(sv[0][0], sv[0][1]), b = fmaxf(sv[1][0], sv[1][1]);
 #pragma unroll
@@ -326,9 +344,48 @@ fwd16_kernel(FwdParams p) {
     const float mx = fmaxf(a, b);
     return fmaxf(mx, other_half(mx));
   };
-  // Offset decision for the coming block's scores, given their raw row max
-  // mx. Returns true (wave-uniform) when some row raised its offset; then
-  // a_cur holds the factor 2^(m_old - m_new) for those rows (1 elsewhere).
+  // P of score pair pp (keys 2pp, 2pp+1 of the lane's 32, in the order of
+  // the P.V B operands) with offset m_off, rounded to the io type and packed
+  auto p_pair = [&](const f32x16(&sv)[2], int pp, float m_off) {
+    const int t = pp / 4, e2 = pp % 4;
+    const float s0 = sv[t / 2][8 * (t % 2) + 2 * e2];
+    const float s1 = sv[t / 2][8 * (t % 2) + 2 * e2 + 1];
+    const f32x2 x = {fast_exp2(fmaf(s0, c, -m_off)), fast_exp2(fmaf(s1, c, -m_off))};
+    return __builtin_convertvector(x, typename Pack2<T>::type);
+  };
+  // Settles the P that a block just computed, before the next block
+  // multiplies it into O: sv are the tile's (masked) scores, pv its P and r
+  // the lane's sum of it.
+  // Common case: every lane's sum is within kSumMax and the row had an
+  // offset, so r joins l. Otherwise the offset is raised to the tile's row
+  // max, O and l are rescaled and the tile's P is recomputed.
+  auto settle = [&](const f32x16(&sv)[2], v8(&pv)[4], float r) {
+    if (__builtin_expect(!__any(r > kSumMax || m_cur == -INFINITY), 1)) {
+      l_run += r;
+      return;
+    }
+    const float m_new = fmaxf(m_cur, row_max(sv) * c);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_cur - m_new);
+    const float m_off = m_new == -INFINITY ? 0.f : m_new;
+    float r0 = 0.f, r1 = 0.f;
+    i32x4 pk[4];
+#pragma unroll
+    for (int pp = 0; pp < NPAIR; ++pp) {
+      const auto h = p_pair(sv, pp, m_off);
+      pk[pp / 4][pp % 4] = __builtin_bit_cast(int, h);
+      if (pp & 1) r1 = dot2_ones<T>(h, r1);
+      else r0 = dot2_ones<T>(h, r0);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pv[t] = __builtin_bit_cast(v8, pk[t]);
+    l_run = l_run * alpha + (r0 + r1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    m_cur = m_new;
+  };
+  // Decided offsets: the decision for the coming block's scores, given their
+  // raw row max mx. Returns true (wave-uniform) when some row raised its
+  // offset; then a_cur holds 2^(m_old - m_new) for those rows (1 elsewhere).
   auto decide = [&](float mx) -> bool {
     const float mt = mx * c;  // log2 units
     const bool need = m_cur == -INFINITY ? mt != -INFINITY : mt > m_cur + kTau;
@@ -343,9 +400,9 @@ fwd16_kernel(FwdParams p) {
   // One pipeline block of step s, straight-line code:
   //   QK  : S_next = K_next Q^T                  (MFMAs 0 .. NQK-1)
   //   PV  : O^T += V_prev^T P_prev^T             (MFMAs NQK .. NM-1)
-  //   SM  : P_cur = 2^(scores), row sum into l   (VALU, early chunks)
-  //   MX  : row max of S_next                    (VALU, last chunks, once the
-  //                                               QK results are complete)
+  //   SM  : P_cur = 2^(c S_cur - m), its sum     (VALU, early chunks)
+  //   MX  : (decided offsets) row max of S_next  (VALU, last chunks, once
+  //                                               the QK results are complete)
   //   MEM : this wave's direct-to-LDS loads of V(s-1+LV) and K(s+1+LK),
   //         one instruction per chunk
   // It is emitted as NM chunks, each = the LDS read for the MFMA PF chunks
@@ -356,9 +413,9 @@ fwd16_kernel(FwdParams p) {
   constexpr int NPV = 4 * (D / 32);
   constexpr int NM = NQK + NPV;
   constexpr int PF = D <= 64 ? 3 : 2;                     // LDS read-ahead (chunks)
-  constexpr int NPAIR = 16;                               // 32 scores per lane, in pairs
-  constexpr int EXP_CHUNKS = NM - 6 < 16 ? NM - 6 : 16;   // chunks holding the exps
-  constexpr int MX0 = NM - 4;                             // chunks MX0 .. MX0+2: max of S_next
+  constexpr int EXP_SPAN = CHECK_AFTER ? NM - 2 : NM - 6;
+  constexpr int EXP_CHUNKS = EXP_SPAN < 16 ? EXP_SPAN : 16;  // chunks holding the exps
+  constexpr int MX0 = NM - 4;  // (decided offsets) chunks MX0 .. MX0+2: max of S_next
   constexpr int MEM0 = 1;                                 // chunks MEM0 .. MEM0+2*CPT-1
   static_assert(MEM0 + 2 * CPT <= NM, "not enough chunks for the memory ops");
   const int vrow = 4 * hf + (lane % 16) / 4;
@@ -389,7 +446,7 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         s_out[mb] = M::mma(read_k(kb, ks, mb), qf[ks], ks == 0 ? f32x16{} : s_out[mb]);
-    mx_nxt = row_max(s_out);
+    if constexpr (!CHECK_AFTER) mx_nxt = row_max(s_out);
   };
   // a wave's last P.V alone (after its last step)
   auto pv_only = [&](const T* vb, const v8(&p_last)[4]) {
@@ -399,7 +456,7 @@ fwd16_kernel(FwdParams p) {
       for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
   };
   auto block = [&](int s, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
-                   v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) {
+                   v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) -> float {
     const T* kb = kbuf0 + ((s + 1) % NBK) * TILE;        // K of step s+1
     const T* vb = vbuf0 + ((s + NBV - 1) % NBV) * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
@@ -420,47 +477,47 @@ fwd16_kernel(FwdParams p) {
         const int p0 = i * NPAIR / EXP_CHUNKS, p1 = (i + 1) * NPAIR / EXP_CHUNKS;
 #pragma unroll
         for (int pp = p0; pp < p1; ++pp) {
-          const int t = pp / 4, e2 = pp % 4;
-          const float s0 = s_cur[t / 2][8 * (t % 2) + 2 * e2];
-          const float s1 = s_cur[t / 2][8 * (t % 2) + 2 * e2 + 1];
-          const f32x2 x = {fast_exp2(fmaf(s0, c, -m_off)), fast_exp2(fmaf(s1, c, -m_off))};
-          const auto h = __builtin_convertvector(x, typename Pack2<T>::type);
+          const auto h = p_pair(s_cur, pp, m_off);
           const int hb = __builtin_bit_cast(int, h);
           pin(hb);
-          pk[t][e2] = hb;
-          if (e2 & 1) r1 = dot2_ones<T>(h, r1);
+          pk[pp / 4][pp % 4] = hb;
+          if (pp & 1) r1 = dot2_ones<T>(h, r1);
           else r0 = dot2_ones<T>(h, r0);
         }
       }
-      if (i == EXP_CHUNKS) {
-        l_run = l_run * a_cur + (r0 + r1);
-        pin(l_run);
-      }
-      if (i == MX0) {
-        mxa = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), s_nxt[0][2]);
-        mxb = fmaxf(fmaxf(s_nxt[0][3], s_nxt[0][4]), s_nxt[0][5]);
-#pragma unroll
-        for (int r = 6; r < 14; r += 4) {
-          mxa = fmaxf(fmaxf(mxa, s_nxt[0][r]), s_nxt[0][r + 1]);
-          mxb = fmaxf(fmaxf(mxb, s_nxt[0][r + 2]), s_nxt[0][r + 3]);
+      if constexpr (CHECK_AFTER) {
+        if (i == EXP_CHUNKS) pin(r0), pin(r1);
+      } else {
+        if (i == EXP_CHUNKS) {
+          l_run = l_run * a_cur + (r0 + r1);
+          pin(l_run);
         }
-        mxa = fmaxf(fmaxf(mxa, s_nxt[0][14]), s_nxt[0][15]);
-        pin(mxa);
-        pin(mxb);
-      }
-      if (i == MX0 + 1) {
+        if (i == MX0) {
+          mxa = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), s_nxt[0][2]);
+          mxb = fmaxf(fmaxf(s_nxt[0][3], s_nxt[0][4]), s_nxt[0][5]);
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          mxa = fmaxf(fmaxf(mxa, s_nxt[1][r]), s_nxt[1][r + 1]);
-          mxb = fmaxf(fmaxf(mxb, s_nxt[1][r + 2]), s_nxt[1][r + 3]);
+          for (int r = 6; r < 14; r += 4) {
+            mxa = fmaxf(fmaxf(mxa, s_nxt[0][r]), s_nxt[0][r + 1]);
+            mxb = fmaxf(fmaxf(mxb, s_nxt[0][r + 2]), s_nxt[0][r + 3]);
+          }
+          mxa = fmaxf(fmaxf(mxa, s_nxt[0][14]), s_nxt[0][15]);
+          pin(mxa);
+          pin(mxb);
         }
-        pin(mxa);
-        pin(mxb);
-      }
-      if (i == MX0 + 2) {
-        const float mx = fmaxf(mxa, mxb);
-        mx_nxt = fmaxf(mx, other_half(mx));
-        pin(mx_nxt);
+        if (i == MX0 + 1) {
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            mxa = fmaxf(fmaxf(mxa, s_nxt[1][r]), s_nxt[1][r + 1]);
+            mxb = fmaxf(fmaxf(mxb, s_nxt[1][r + 2]), s_nxt[1][r + 3]);
+          }
+          pin(mxa);
+          pin(mxb);
+        }
+        if (i == MX0 + 2) {
+          const float mx = fmaxf(mxa, mxb);
+          mx_nxt = fmaxf(mx, other_half(mx));
+          pin(mx_nxt);
+        }
       }
     };
     v8 op[NM];
@@ -482,6 +539,7 @@ fwd16_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) p_cur[t] = __builtin_bit_cast(v8, pk[t]);
+    return r0 + r1;
   };
 
   // The start of step s, common to every wave: the descriptors of the tiles
@@ -505,30 +563,45 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
     for (int x = 0; x < CPT; ++x) kdma(rk, s + 1 + LK, x);
   };
-  // Step s with a block: the offset decision for the wave's tile of step s,
-  // then the fused block. Every block runs the same code; the first block's
-  // P.V is neutralised by data (P_prev = 0), and the last block's QK of the
-  // next tile computes a value that is never used.
-  auto step = [&](int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
-                  v8(&p_cur)[4]) {
+  // Step s with a block: the mask of this tile's scores where a band bound
+  // cuts it, then the fused block with the offset checked after it (or
+  // decided before it, with the O rescale after it). Every block runs the
+  // same code; the first block's P.V is neutralised by
+  // data (P_prev = 0), and the last block's QK of the next tile computes a
+  // value that is never used.
+  // (FIRST: the wave's first tile, a separate instantiation so that the row
+  // max it takes, and the canonicalisation of the masked scores that it
+  // needs, stay out of the other steps)
+  auto step = [&](auto first, int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+                  const v8(&p_prev)[4], v8(&p_cur)[4]) {
+    constexpr bool FIRST = decltype(first)::value;
     i32x4 rk, rv;
     step_begin(s, rk, rv);
     const int kbase = (t0 + s) * BN;  // this step's key tile
-    float mx = mx_nxt;
     const bool cut_causal = CAUSAL && kbase + BN - 1 > row0 + shift;
     const bool cut_left = kbase < wave_last + shift - window;
     const bool cut_end = kbase + BN > kv_len;
-    if (cut_causal || cut_left || cut_end) {
-      mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
-                        cut_end);
-      mx = row_max(s_cur);
-    }
-    const bool rescale = decide(mx);
-    const float a_blk = a_cur;
-    block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
-    if (rescale) {
+    if constexpr (CHECK_AFTER) {
+      if (cut_causal || cut_left || cut_end)
+        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
+                          cut_end);
+      if constexpr (FIRST) m_cur = row_max(s_cur) * c;  // the first tile's own row max
+      const float r = block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+      settle(s_cur, p_cur, r);  // before the next block multiplies P_cur into O
+    } else {
+      float mx = mx_nxt;
+      if (cut_causal || cut_left || cut_end) {
+        mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
+                          cut_end);
+        mx = row_max(s_cur);
+      }
+      const bool rescale = decide(mx);
+      const float a_blk = a_cur;
+      block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+      if (rescale) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
+        for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
+      }
     }
   };
 
@@ -622,16 +695,33 @@ fwd16_kernel(FwdParams p) {
   }
   // this wave's steps: even offsets from ws0 use S_cur = sa, S_next = sb,
   // P_prev = pb, P_cur = pa; odd ones the other way round
+  using kFirst = std::true_type;
+  using kNext = std::false_type;
   bool last_in_pa = true;
   if (ws1 > ws0) {
-    for (; s + 1 < ws1; s += 2) {
-      step(s, sa, sb, pb, pa);
-      step(s + 1, sb, sa, pa, pb);
-    }
-    last_in_pa = s < ws1;
-    if (s < ws1) {
-      step(s, sa, sb, pb, pa);
+    if constexpr (CHECK_AFTER) {
+      // the first step on its own, then pairs from an odd offset
+      step(kFirst{}, s, sa, sb, pb, pa);
       ++s;
+      for (; s + 1 < ws1; s += 2) {
+        step(kNext{}, s, sb, sa, pa, pb);
+        step(kNext{}, s + 1, sa, sb, pb, pa);
+      }
+      last_in_pa = s >= ws1;
+      if (s < ws1) {
+        step(kNext{}, s, sb, sa, pa, pb);
+        ++s;
+      }
+    } else {
+      for (; s + 1 < ws1; s += 2) {
+        step(kNext{}, s, sa, sb, pb, pa);
+        step(kNext{}, s + 1, sb, sa, pa, pb);
+      }
+      last_in_pa = s < ws1;
+      if (s < ws1) {
+        step(kNext{}, s, sa, sb, pb, pa);
+        ++s;
+      }
     }
   }
   // the P.V of the wave's last tile (its V is intact until two steps later),

@@ -66,6 +66,34 @@ def test_scale_sign_and_zero(gpu, scale):
         check_lse(f64(lse), lse_ref)
 
 
+RISING = [
+    # dtype, s_q, s_kv, d, causal
+    ("bf16", 300, 300, 64, True),
+    ("fp16", 200, 520, 64, False),
+    ("bf16", 257, 257, 128, True),
+    ("fp16", 130, 390, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", RISING, ids=lambda c: "-".join(map(str, c)))
+def test_rising_scores_raise_offsets(gpu, case):
+    """Key rows scaled up along the sequence (x1 .. x24), so that the scores of
+    later key tiles rise tens of log2 units above the first tile's: the P of
+    such tiles overflow the offset taken so far (past the 16-bit range for
+    fp16), and every such tile must raise the row's offset and rescale O and
+    l before its P.V. The oracle computes the definition directly."""
+    dt, sq, skv, d, causal = case
+    announce(f"fwd rising scores {case}")
+    q, k, v = W.dense_inputs(1, 2, sq, skv, d, dt, "bhsd", seed=401 + skv + d)
+    ramp = 1.0 + 23.0 * torch.arange(skv, dtype=torch.float32) / max(skv - 1, 1)
+    k = (k.float() * ramp[None, None, :, None]).to(k.dtype)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = _run(q, k, v, scale, causal, gpu)
+    o_ref, lse_ref = oracle.fwd(f64(q), f64(k), f64(v), scale, causal)
+    check_o(f64(o), o_ref, dt)
+    check_lse(f64(lse), lse_ref)
+
+
 def test_no_keys_gives_dead_rows(gpu):
     import scaled_dot_product_07_amd as sdpa
     announce("fwd s_kv=0")
