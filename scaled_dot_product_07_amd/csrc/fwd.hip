@@ -353,35 +353,47 @@ fwd16_kernel(FwdParams p) {
     const f32x2 x = {fast_exp2(fmaf(s0, c, -m_off)), fast_exp2(fmaf(s1, c, -m_off))};
     return __builtin_convertvector(x, typename Pack2<T>::type);
   };
-  // Settles the P that a block just computed, before the next block
-  // multiplies it into O: sv are the tile's (masked) scores, pv its P and r
-  // the lane's sum of it.
-  // Common case: every lane's sum is within kSumMax and the row had an
-  // offset, so r joins l. Otherwise the offset is raised to the tile's row
-  // max, O and l are rescaled and the tile's P is recomputed.
-  auto settle = [&](const f32x16(&sv)[2], v8(&pv)[4], float r) {
-    if (__builtin_expect(!__any(r > kSumMax || m_cur == -INFINITY), 1)) {
-      l_run += r;
-      return;
-    }
+  // Settling the P that a block just computed, before the next block
+  // multiplies it into O (sv: the tile's masked scores, pv: its P, r: the
+  // lane's sum of it). p_ok: every lane's sum is within kSumMax and the row
+  // had an offset, so r joins l. Otherwise fix raises the offset to the
+  // tile's row max, rescales O and l and recomputes the tile's P.
+  auto p_ok = [&](float r) -> bool { return !__any(r > kSumMax || m_cur == -INFINITY); };
+  auto fix = [&](const f32x16(&sv)[2], v8(&pv)[4]) {
     const float m_new = fmaxf(m_cur, row_max(sv) * c);
     const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_cur - m_new);
     const float m_off = m_new == -INFINITY ? 0.f : m_new;
+    // P and O are rewritten in place, pair by pair (operands tied to their
+    // own registers, no temporaries)
     float r0 = 0.f, r1 = 0.f;
-    i32x4 pk[4];
 #pragma unroll
-    for (int pp = 0; pp < NPAIR; ++pp) {
-      const auto h = p_pair(sv, pp, m_off);
-      pk[pp / 4][pp % 4] = __builtin_bit_cast(int, h);
-      if (pp & 1) r1 = dot2_ones<T>(h, r1);
-      else r0 = dot2_ones<T>(h, r0);
+    for (int t = 0; t < 4; ++t) {
+      i32x4 w = __builtin_bit_cast(i32x4, pv[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto h = p_pair(sv, 4 * t + e, m_off);
+        if (e & 1) r1 = dot2_ones<T>(h, r1);
+        else r0 = dot2_ones<T>(h, r0);
+        int o = w[e];
+        asm volatile("v_mov_b32 %0, %1" : "+v"(o) : "v"(__builtin_bit_cast(int, h)));
+        w[e] = o;
+      }
+      pv[t] = __builtin_bit_cast(v8, w);
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) pv[t] = __builtin_bit_cast(v8, pk[t]);
     l_run = l_run * alpha + (r0 + r1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = acc[db][e];
+        asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+        acc[db][e] = x;
+      }
     m_cur = m_new;
+  };
+  auto settle = [&](const f32x16(&sv)[2], v8(&pv)[4], float r) {
+    if (__builtin_expect(p_ok(r), 1)) l_run += r;
+    else fix(sv, pv);
   };
   // Decided offsets: the decision for the coming block's scores, given their
   // raw row max mx. Returns true (wave-uniform) when some row raised its
@@ -564,8 +576,9 @@ fwd16_kernel(FwdParams p) {
     for (int x = 0; x < CPT; ++x) kdma(rk, s + 1 + LK, x);
   };
   // Step s with a block: the mask of this tile's scores where a band bound
-  // cuts it, then the fused block with the offset checked after it (or
-  // decided before it, with the O rescale after it). Every block runs the
+  // cuts it, then the fused block; with checked offsets it returns the
+  // lane's sum of the P it computed, for the caller to settle (with decided
+  // offsets the decision comes before the block and the O rescale after it). Every block runs the
   // same code; the first block's P.V is neutralised by
   // data (P_prev = 0), and the last block's QK of the next tile computes a
   // value that is never used.
@@ -573,7 +586,7 @@ fwd16_kernel(FwdParams p) {
   // max it takes, and the canonicalisation of the masked scores that it
   // needs, stay out of the other steps)
   auto step = [&](auto first, int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
-                  const v8(&p_prev)[4], v8(&p_cur)[4]) {
+                  const v8(&p_prev)[4], v8(&p_cur)[4]) -> float {
     constexpr bool FIRST = decltype(first)::value;
     i32x4 rk, rv;
     step_begin(s, rk, rv);
@@ -586,8 +599,7 @@ fwd16_kernel(FwdParams p) {
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
       if constexpr (FIRST) m_cur = row_max(s_cur) * c;  // the first tile's own row max
-      const float r = block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
-      settle(s_cur, p_cur, r);  // before the next block multiplies P_cur into O
+      return block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
     } else {
       float mx = mx_nxt;
       if (cut_causal || cut_left || cut_end) {
@@ -602,6 +614,7 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
       }
+      return 0.f;
     }
   };
 
@@ -700,16 +713,41 @@ fwd16_kernel(FwdParams p) {
   bool last_in_pa = true;
   if (ws1 > ws0) {
     if constexpr (CHECK_AFTER) {
-      // the first step on its own, then pairs from an odd offset
-      step(kFirst{}, s, sa, sb, pb, pa);
+      // the first step on its own, then pairs from an odd offset. A tile
+      // whose P needs a new offset leaves the inner loop and is fixed
+      // outside it (with the rest of its pair), so that the loop's code
+      // holds no O rescale: one inside it made the register allocator move
+      // O and P between two register sets, with a copy of both every step.
+      settle(sa, pa, step(kFirst{}, s, sa, sb, pb, pa));
       ++s;
-      for (; s + 1 < ws1; s += 2) {
-        step(kNext{}, s, sb, sa, pa, pb);
-        step(kNext{}, s + 1, sa, sb, pb, pa);
+      while (s + 1 < ws1) {
+        int ev = 0;  // 1: the pair's first tile needs fixing, 2: its second
+        for (; s + 1 < ws1; s += 2) {
+          const float ra = step(kNext{}, s, sb, sa, pa, pb);
+          if (__builtin_expect(!p_ok(ra), 0)) {
+            ev = 1;
+            break;
+          }
+          l_run += ra;
+          const float rb = step(kNext{}, s + 1, sa, sb, pb, pa);
+          if (__builtin_expect(!p_ok(rb), 0)) {
+            ev = 2;
+            break;
+          }
+          l_run += rb;
+        }
+        if (ev == 0) break;
+        if (ev == 1) {
+          fix(sb, pb);  // tile s: scores in sb, P in pb
+          settle(sa, pa, step(kNext{}, s + 1, sa, sb, pb, pa));
+        } else {
+          fix(sa, pa);  // tile s + 1: scores in sa, P in pa
+        }
+        s += 2;
       }
       last_in_pa = s >= ws1;
       if (s < ws1) {
-        step(kNext{}, s, sb, sa, pa, pb);
+        settle(sb, pb, step(kNext{}, s, sb, sa, pa, pb));
         ++s;
       }
     } else {

@@ -94,6 +94,26 @@ def test_rising_scores_raise_offsets(gpu, case):
     check_lse(f64(lse), lse_ref)
 
 
+@pytest.mark.parametrize("parity", [0, 1])
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("fp16", False)])
+def test_rises_on_alternate_key_tiles(gpu, parity, dt, causal):
+    """Scores that jump up only on every other 64-key tile (the rest scaled
+    down), so that the offset has to be raised on tiles of one parity of the
+    key loop only: after the first tile of a pair of steps, or after the
+    second, in turn for the two parities."""
+    announce(f"fwd alternating rises parity={parity} {dt} causal={causal}")
+    s, d = 460, 64
+    q, k, v = W.dense_inputs(1, 2, s, s, d, dt, "bhsd", seed=433 + parity)
+    tile = torch.arange(s) // 64
+    f = torch.where(tile % 2 == parity, 1.0 + 5.0 * tile.float(), torch.full((s,), 0.5))
+    k = (k.float() * f[None, None, :, None]).to(k.dtype)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = _run(q, k, v, scale, causal, gpu)
+    o_ref, lse_ref = oracle.fwd(f64(q), f64(k), f64(v), scale, causal)
+    check_o(f64(o), o_ref, dt)
+    check_lse(f64(lse), lse_ref)
+
+
 def test_no_keys_gives_dead_rows(gpu):
     import scaled_dot_product_07_amd as sdpa
     announce("fwd s_kv=0")
