@@ -467,10 +467,14 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
   };
-  auto block = [&](int s, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2], const v8(&p_prev)[4],
+  static_assert(NBK == 2 && NBV == 2, "the blocks read buffer (s + 1) mod 2 of K and of V");
+  // rbuf = (s + 1) mod 2, passed in so that a loop over pairs of steps keeps
+  // the LDS operand addresses of both steps loop-invariant
+  auto block = [&](int s, int rbuf, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+                   const v8(&p_prev)[4],
                    v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) -> float {
-    const T* kb = kbuf0 + ((s + 1) % NBK) * TILE;        // K of step s+1
-    const T* vb = vbuf0 + ((s + NBV - 1) % NBV) * TILE;  // V of step s-1
+    const T* kb = kbuf0 + rbuf * TILE;  // K of step s+1
+    const T* vb = vbuf0 + rbuf * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
       if (i < NQK) return read_k(kb, i / 2, i % 2);
       return read_v(vb, (i - NQK) / (D / 32), (i - NQK) % (D / 32));
@@ -585,7 +589,7 @@ fwd16_kernel(FwdParams p) {
   // (FIRST: the wave's first tile, a separate instantiation so that the row
   // max it takes, and the canonicalisation of the masked scores that it
   // needs, stay out of the other steps)
-  auto step = [&](auto first, int s, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+  auto step = [&](auto first, int s, int rbuf, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
                   const v8(&p_prev)[4], v8(&p_cur)[4]) -> float {
     constexpr bool FIRST = decltype(first)::value;
     i32x4 rk, rv;
@@ -599,7 +603,7 @@ fwd16_kernel(FwdParams p) {
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
       if constexpr (FIRST) m_cur = row_max(s_cur) * c;  // the first tile's own row max
-      return block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
+      return block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
     } else {
       float mx = mx_nxt;
       if (cut_causal || cut_left || cut_end) {
@@ -609,7 +613,7 @@ fwd16_kernel(FwdParams p) {
       }
       const bool rescale = decide(mx);
       const float a_blk = a_cur;
-      block(s, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+      block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);
       if (rescale) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
@@ -718,18 +722,19 @@ fwd16_kernel(FwdParams p) {
       // outside it (with the rest of its pair), so that the loop's code
       // holds no O rescale: one inside it made the register allocator move
       // O and P between two register sets, with a copy of both every step.
-      settle(sa, pa, step(kFirst{}, s, sa, sb, pb, pa));
+      settle(sa, pa, step(kFirst{}, s, (s + 1) & 1, sa, sb, pb, pa));
       ++s;
       while (s + 1 < ws1) {
         int ev = 0;  // 1: the pair's first tile needs fixing, 2: its second
+        const int ba = (s + 1) & 1;  // the pairs' first steps read buffer ba
         for (; s + 1 < ws1; s += 2) {
-          const float ra = step(kNext{}, s, sb, sa, pa, pb);
+          const float ra = step(kNext{}, s, ba, sb, sa, pa, pb);
           if (__builtin_expect(!p_ok(ra), 0)) {
             ev = 1;
             break;
           }
           l_run += ra;
-          const float rb = step(kNext{}, s + 1, sa, sb, pb, pa);
+          const float rb = step(kNext{}, s + 1, ba ^ 1, sa, sb, pb, pa);
           if (__builtin_expect(!p_ok(rb), 0)) {
             ev = 2;
             break;
@@ -739,7 +744,7 @@ fwd16_kernel(FwdParams p) {
         if (ev == 0) break;
         if (ev == 1) {
           fix(sb, pb);  // tile s: scores in sb, P in pb
-          settle(sa, pa, step(kNext{}, s + 1, sa, sb, pb, pa));
+          settle(sa, pa, step(kNext{}, s + 1, (s + 2) & 1, sa, sb, pb, pa));
         } else {
           fix(sa, pa);  // tile s + 1: scores in sa, P in pa
         }
@@ -747,17 +752,18 @@ fwd16_kernel(FwdParams p) {
       }
       last_in_pa = s >= ws1;
       if (s < ws1) {
-        settle(sb, pb, step(kNext{}, s, sb, sa, pa, pb));
+        settle(sb, pb, step(kNext{}, s, (s + 1) & 1, sb, sa, pa, pb));
         ++s;
       }
     } else {
+      const int ba = (s + 1) & 1;
       for (; s + 1 < ws1; s += 2) {
-        step(kNext{}, s, sa, sb, pb, pa);
-        step(kNext{}, s + 1, sb, sa, pa, pb);
+        step(kNext{}, s, ba, sa, sb, pb, pa);
+        step(kNext{}, s + 1, ba ^ 1, sb, sa, pa, pb);
       }
       last_in_pa = s < ws1;
       if (s < ws1) {
-        step(kNext{}, s, sa, sb, pb, pa);
+        step(kNext{}, s, (s + 1) & 1, sa, sb, pb, pa);
         ++s;
       }
     }
