@@ -48,6 +48,7 @@
 // tiles of one (b, h) run on the same XCD when b*h is a multiple of 8 and
 // share its L2.
 
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -294,11 +295,23 @@ fwd16_kernel(FwdParams p) {
   const T* __restrict__ K0 = K + (int64_t)t0 * BN * p.k_ss;
   const T* __restrict__ V0 = V + (int64_t)t0 * BN * p.v_ss;
   const int kv_rel = kv_end - t0 * BN;  // keys from tile t0 on
-  auto tile_rsrc_at = [&](const T* __restrict__ tb, int64_t stride, int t) -> i32x4 {
-    const int rows = t < 0 ? 0 : min(kv_rel - t * BN, BN);
-    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
+  // tiles 0 .. n_full-1 (from t0) hold BN keys, tile n_full the remaining
+  // kv_rel mod BN (if any), later tiles none
+  const int n_full = kv_rel / BN, edge_rows = kv_rel % BN;
+  auto tile_bytes = [&](int64_t stride, int rows) -> int {
+    return rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
+  };
+  const int full_k = tile_bytes(p.k_ss, BN), edge_k = tile_bytes(p.k_ss, edge_rows);
+  const int full_v = tile_bytes(p.v_ss, BN), edge_v = tile_bytes(p.v_ss, edge_rows);
+  auto tile_bytes_at = [&](int t, int full, int edge) -> int {
+    return (t < 0 || t > n_full) ? 0 : t < n_full ? full : edge;
+  };
+  auto make_rsrc = [&](const T* __restrict__ tb, int bytes) -> i32x4 {
     const unsigned long long a = (unsigned long long)tb;
     return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
+  };
+  auto tile_rsrc_at = [&](const T* __restrict__ tb, int t, int full, int edge) -> i32x4 {
+    return make_rsrc(tb, tile_bytes_at(t, full, edge));
   };
   auto dma = [&](i32x4 rs, int voff, int soff, T* dst) {
     lds_dma16(rs, voff, soff,
@@ -306,16 +319,19 @@ fwd16_kernel(FwdParams p) {
   };
   // this wave's load instruction x of tile u's K (V) into its buffer (u >= -1;
   // tile -1 is all zeros)
-  auto kdma = [&](i32x4 r, int u, int x) {
-    dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T),
-        kbuf0 + (u % NBK) * TILE + RIT(x) * D);
+  // (the buffer index: u mod NBK for K tile u, (u + NBV) mod NBV for V tile
+  // u >= -1; the fused blocks pass it in as a loop-invariant value)
+  auto kdma = [&](i32x4 r, int buf, int x) {
+    dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T), kbuf0 + buf * TILE + RIT(x) * D);
   };
-  auto vdma = [&](i32x4 r, int u, int x) {
-    dma(r, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T),
-        vbuf0 + ((u + NBV) % NBV) * TILE + RIT(x) * D);
+  auto vdma = [&](i32x4 r, int buf, int x) {
+    dma(r, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T), vbuf0 + buf * TILE + RIT(x) * D);
   };
-  auto rsrc = [&](const T* __restrict__ base, int64_t stride, int u) -> i32x4 {
-    return tile_rsrc_at(base + (int64_t)u * BN * stride, stride, u);
+  auto rsrc_k = [&](int u) -> i32x4 {
+    return tile_rsrc_at(K0 + (int64_t)u * BN * p.k_ss, u, full_k, edge_k);
+  };
+  auto rsrc_v = [&](int u) -> i32x4 {
+    return tile_rsrc_at(V0 + (int64_t)u * BN * p.v_ss, u, full_v, edge_v);
   };
   // first rows of the tiles the next step's loads fill (K of step s+1+LK,
   // V of step s-1+LV), advanced by one tile of rows per step so that the
@@ -482,8 +498,9 @@ fwd16_kernel(FwdParams p) {
     auto mem = [&](int i) {  // loads of V(s-1+LV), then K(s+1+LK)
       const int k = i - MEM0;
       if (k < 0 || k >= 2 * CPT) return;
-      if (k < CPT) vdma(rv, s - 1 + LV, k);
-      else kdma(rk, s + 1 + LK, k - CPT);
+      // V(s - 1 + LV) and K(s + 1 + LK) both go to buffer s mod 2 = rbuf ^ 1
+      if (k < CPT) vdma(rv, rbuf ^ 1, k);
+      else kdma(rk, rbuf ^ 1, k - CPT);
     };
     const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
     float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
@@ -563,21 +580,42 @@ fwd16_kernel(FwdParams p) {
   // step reads, and one barrier (every wave's loads have then landed, and
   // every wave is done with the buffers this step's loads overwrite).
   auto step_begin = [&](int s, i32x4& rk, i32x4& rv) {
-    rk = tile_rsrc_at(kstep_ptr, p.k_ss, s + 1 + LK);
-    rv = tile_rsrc_at(vstep_ptr, p.v_ss, s - 1 + LV);
+    // both tiles whole unless one is past the keys' last full tile (or
+    // before the first)
+    const int tk = s + 1 + LK, tv = s - 1 + LV;
+    int bk = full_k, bv = full_v;
+    if (__builtin_expect(tk >= n_full || tv < 0, 0)) {
+      bk = tile_bytes_at(tk, full_k, edge_k);
+      bv = tile_bytes_at(tv, full_v, edge_v);
+    }
+    rk = make_rsrc(kstep_ptr, bk);
+    rv = make_rsrc(vstep_ptr, bv);
     kstep_ptr += BN * p.k_ss;
     vstep_ptr += BN * p.v_ss;
     wait_vm(WaitStep{});
     __builtin_amdgcn_s_barrier();
   };
+  // No band bound cuts the tile with first key kbase iff kbase lies in
+  // [uncut_lo, uncut_hi]: the left bound cuts it when kbase < uncut_lo, the
+  // causal bound when kbase > row0 + shift - BN + 1, the end of the keys when
+  // kbase > kv_len - BN. One unsigned compare per step tests the interval
+  // (an empty interval makes every tile cut: kbase >= 0 > INT_MIN).
+  int uncut_lo = wave_last + shift - window;
+  int uncut_hi = kv_len - BN;
+  if (CAUSAL) uncut_hi = min(uncut_hi, row0 + shift - BN + 1);
+  unsigned uncut_span = (unsigned)uncut_hi - (unsigned)uncut_lo;
+  if (uncut_hi < uncut_lo) {
+    uncut_lo = INT_MIN;
+    uncut_span = 0u;
+  }
   // A step without a block: the wave's share of the step's loads only.
   auto light_step = [&](int s) {
     i32x4 rk, rv;
     step_begin(s, rk, rv);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) vdma(rv, s - 1 + LV, x);
+    for (int x = 0; x < CPT; ++x) vdma(rv, (s - 1 + LV + NBV) % NBV, x);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) kdma(rk, s + 1 + LK, x);
+    for (int x = 0; x < CPT; ++x) kdma(rk, (s + 1 + LK) % NBK, x);
   };
   // Step s with a block: the mask of this tile's scores where a band bound
   // cuts it, then the fused block; with checked offsets it returns the
@@ -595,18 +633,19 @@ fwd16_kernel(FwdParams p) {
     i32x4 rk, rv;
     step_begin(s, rk, rv);
     const int kbase = (t0 + s) * BN;  // this step's key tile
+    const bool any_cut = (unsigned)kbase - (unsigned)uncut_lo > uncut_span;
     const bool cut_causal = CAUSAL && kbase + BN - 1 > row0 + shift;
     const bool cut_left = kbase < wave_last + shift - window;
     const bool cut_end = kbase + BN > kv_len;
     if constexpr (CHECK_AFTER) {
-      if (cut_causal || cut_left || cut_end)
+      if (any_cut)
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
       if constexpr (FIRST) m_cur = row_max(s_cur) * c;  // the first tile's own row max
       return block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
     } else {
       float mx = mx_nxt;
-      if (cut_causal || cut_left || cut_end) {
+      if (any_cut) {
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
         mx = row_max(s_cur);
@@ -676,13 +715,13 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
   for (int b = -(LK + 1); b < 0; ++b) {
     if (b - 1 + LV >= -1) {
-      const i32x4 r = rsrc(V0, p.v_ss, b - 1 + LV);
+      const i32x4 r = rsrc_v(b - 1 + LV);
 #pragma unroll
-      for (int x = 0; x < CPT; ++x) vdma(r, b - 1 + LV, x);
+      for (int x = 0; x < CPT; ++x) vdma(r, (b - 1 + LV + NBV) % NBV, x);
     }
-    const i32x4 r = rsrc(K0, p.k_ss, b + 1 + LK);
+    const i32x4 r = rsrc_k(b + 1 + LK);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) kdma(r, b + 1 + LK, x);
+    for (int x = 0; x < CPT; ++x) kdma(r, (b + 1 + LK) % NBK, x);
   }
   static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
   f32x16 sa[2], sb[2];
