@@ -303,6 +303,8 @@ fwd16_kernel(FwdParams p) {
   };
   const int full_k = tile_bytes(p.k_ss, BN), edge_k = tile_bytes(p.k_ss, edge_rows);
   const int full_v = tile_bytes(p.v_ss, BN), edge_v = tile_bytes(p.v_ss, edge_rows);
+  static_assert(LV == 1 && LK == 1, "step loads: V of the step's own tile, K two tiles ahead");
+  const int s_edge = n_full - 1 - LK;  // first step whose K tile is not a whole one
   auto tile_bytes_at = [&](int t, int full, int edge) -> int {
     return (t < 0 || t > n_full) ? 0 : t < n_full ? full : edge;
   };
@@ -374,7 +376,9 @@ fwd16_kernel(FwdParams p) {
   // lane's sum of it). p_ok: every lane's sum is within kSumMax and the row
   // had an offset, so r joins l. Otherwise fix raises the offset to the
   // tile's row max, rescales O and l and recomputes the tile's P.
-  auto p_ok = [&](float r) -> bool { return !__any(r > kSumMax || m_cur == -INFINITY); };
+  auto p_ok = [&](float r) -> bool {
+    return __builtin_amdgcn_ballot_w64(r > kSumMax || m_cur == -INFINITY) == 0;
+  };
   auto fix = [&](const f32x16(&sv)[2], v8(&pv)[4]) {
     const float m_new = fmaxf(m_cur, row_max(sv) * c);
     const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_cur - m_new);
@@ -580,11 +584,11 @@ fwd16_kernel(FwdParams p) {
   // step reads, and one barrier (every wave's loads have then landed, and
   // every wave is done with the buffers this step's loads overwrite).
   auto step_begin = [&](int s, i32x4& rk, i32x4& rv) {
-    // both tiles whole unless one is past the keys' last full tile (or
-    // before the first)
+    // both tiles whole unless the later one (K, tile s + 2) reaches the
+    // keys' edge tile (the V tile, s, is never before the first)
     const int tk = s + 1 + LK, tv = s - 1 + LV;
     int bk = full_k, bv = full_v;
-    if (__builtin_expect(tk >= n_full || tv < 0, 0)) {
+    if (__builtin_expect(s >= s_edge, 0)) {
       bk = tile_bytes_at(tk, full_k, edge_k);
       bv = tile_bytes_at(tv, full_v, edge_v);
     }
