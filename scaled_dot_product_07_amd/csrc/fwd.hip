@@ -6,18 +6,20 @@
 // top-left causal band; cudnn-frontend PR #554: statistic layouts and THD
 // packing with cu_seqlens).
 //
-// fp16/bf16: one workgroup = 8 waves = one 128-row query tile of one
-// (b, h) or (sequence, h) (for causal attention: a pair of query tiles, one
-// after the other). Each wave owns 32 query rows and half of the key tiles
-// (waves w and w+4 split the keys of the same rows) and keeps, for the whole
-// key loop:
+// fp16/bf16: one workgroup = 8 waves over two 128-row query tiles of one
+// (b, h) or (sequence, h): waves 0-3 hold the rows of the first tile, 4-7
+// those of the second, 32 rows each, so every SIMD hosts one wave of each
+// (for a causal band without a left bound the tiles are paired heavy with
+// light, (n-1-i, i)). Each wave keeps, for its whole key range:
 //   * its Q rows as MFMA B operands in VGPRs,
 //   * the fp32 output accumulator O^T (d x 32) in the MFMA C layout,
 //   * the offset m and running sum l of its rows.
-// Keys are streamed in tiles of 64 rows of K and V, loaded by the buffer
-// loads' direct-to-LDS path into double-buffered LDS one step ahead of the
-// block that reads them, with one barrier per step (two tiles). The two
-// key-group partial results of a row are merged through LDS at the end.
+// Keys are streamed in tiles of 64 rows of K and V shared by all eight
+// waves, loaded by the buffer loads' direct-to-LDS path into double-buffered
+// LDS one step ahead of the block that reads them, with one barrier per
+// step. A wave computes over the steps its rows reach and only loads and
+// waits at the others; each wave sees every key tile of its rows, so no
+// partial results are merged.
 // fp32 io: 4 waves, 128 rows, one tile per step, loads through VGPRs.
 //
 // The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, on
@@ -30,10 +32,11 @@
 // by the transposing LDS read ds_read_b64_tr_b16), so P never goes through
 // LDS.
 //
-// Online softmax in base 2: c = |scale| * log2(e), m' = max(m, c * rowmax S),
-// P = 2^(c*S - m'), alpha = 2^(m - m'), l' = alpha*l + rowsum P,
-// O' = alpha*O + P V; at the end O = O / l and LSE = ln2 * (m + log2 l).
-// A negative scale is moved onto Q as an exact sign flip so that c > 0.
+// Online softmax in base 2 with c = |scale| * log2(e): P = 2^(c*S - m) with
+// a row offset m that is raised lazily (see kSumMax below), alpha =
+// 2^(m_old - m_new) rescales l and O when it is, and at the end O = O / l
+// and LSE = ln2 * (m + log2 l). A negative scale is moved onto Q as an exact
+// sign flip so that c > 0.
 //
 // Causal (top-left): query i sees key j iff j <= i. Key tiles past the last
 // visible key of the workgroup are never loaded; a wave skips the tiles past
