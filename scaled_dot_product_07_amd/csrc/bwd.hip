@@ -627,23 +627,13 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
         for (int r = 0; r < 16; ++r) dp[r] = sv[r] * (dp[r] - dl);
         v8 sb[2];
         pack_b1<T>(dp, sb);
-        {
-          // dQ^T += K^T dS^T: operand i = (key half t = i / NB, d block
-          // db = i % NB), read kDqPF MFMAs ahead
-          constexpr int NB = D / 32, N = 2 * NB;
-          auto rd = [&](int i) -> v8 {
-            return read_tr<T, PITCH>(kb_, 16 * (2 * kb + i / NB) + vrow, 32 * (i % NB) + vcol);
-          };
-          v8 a[N];
 #pragma unroll
-          for (int i = 0; i < kDqPF; ++i) a[i] = rd(i);
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < N; ++i) {
-            if (i + kDqPF < N) a[i + kDqPF] = rd(i + kDqPF);
-            dq[i % NB] = M::mma(a[i], sb[i / NB], dq[i % NB]);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int db = 0; db < D / 32; ++db) {
+            const v8 ak = read_tr<T, PITCH>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol);
+            dq[db] = M::mma(ak, sb[t], dq[db]);
           }
-        }
       }
     }
     if (j + 1 < j1) {
