@@ -55,8 +55,6 @@ constexpr int kDkdvQ = 64;      // queries per streamed tile
 constexpr int kDqRows = 128;    // queries per dQ workgroup (32 per wave)
 constexpr int kDqK = 64;        // keys per streamed tile
 constexpr int kNoWindow = 1 << 29;  // window_left = -1: a left bound no key reaches
-constexpr int kBwdPF = 3;           // LDS operand read-ahead of the dK/dV products (MFMAs)
-constexpr int kDqPF = 2;            // the same for the S and dP products of the dQ pass
 
 template <typename T>
 __device__ __forceinline__ float to_f(T x) {
@@ -327,40 +325,29 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
   // acc += A2^T X over the 64 queries of a tile, A2^T read through the
   // transposing LDS read (dO^T for dV, Q^T for dK)
-  // (both products read their LDS operands kBwdPF MFMAs ahead, in an order
-  // pinned per MFMA, so that an MFMA rarely waits for its operand)
   auto accumulate = [&](const T* a2, const f32x16 (&x)[2]) {
     v8 xb[4];
     pack_b<T>(x, xb);
-    constexpr int NB = D / 32, N = 4 * NB;
-    auto rd = [&](int i) -> v8 { return read_tr<T, PITCH>(a2, 16 * (i / NB) + vrow, 32 * (i % NB) + vcol); };
-    v8 a[N];
 #pragma unroll
-    for (int i = 0; i < kBwdPF; ++i) a[i] = rd(i);
+    for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i + kBwdPF < N) a[i + kBwdPF] = rd(i + kBwdPF);
-      acc[i % NB] = M::mma(a[i], xb[i / NB], acc[i % NB]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int db = 0; db < D / 32; ++db) {
+        const v8 a = read_tr<T, PITCH>(a2, 16 * t4 + vrow, 32 * db + vcol);
+        acc[db] = M::mma(a, xb[t4], acc[db]);
+      }
   };
   // x = A1 B over the d columns, A1 rows read from LDS (Q for S, dO for dP);
   // C layout: lane = key kj, register r of block qb = query
   // t*BQ + 32qb + 8(r/4) + 4hf + r%4
   auto product = [&](const T* a1, f32x16 (&x)[2]) {
-    constexpr int NK = D / 16, N = 2 * NK;
-    auto rd = [&](int i) -> v8 {
-      return *(const v8*)&a1[(32 * (i / NK) + col) * PITCH + 16 * (i % NK) + 8 * hf];
-    };
-    v8 a[N];
 #pragma unroll
-    for (int i = 0; i < kBwdPF; ++i) a[i] = rd(i);
+    for (int qb = 0; qb < 2; ++qb) {
+      x[qb] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i + kBwdPF < N) a[i + kBwdPF] = rd(i + kBwdPF);
-      const int qb = i / NK, ks = i % NK;
-      x[qb] = M::mma(a[i], bf[ks], ks == 0 ? f32x16{} : x[qb]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const v8 a = *(const v8*)&a1[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
+        x[qb] = M::mma(a, bf[ks], x[qb]);
+      }
     }
   };
 
@@ -585,24 +572,12 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 sv = {}, dp = {};
-        {
-          // operand i: K (even i) or V (odd i) row block, d slice ks = i / 2,
-          // read kDqPF MFMAs ahead in an order pinned per MFMA
-          constexpr int N = 2 * (D / 16);
-          auto rd = [&](int i) -> v8 {
-            const T* src = (i & 1) ? vb_ : kb_;
-            return *(const v8*)&src[(32 * kb + col) * PITCH + 16 * (i / 2) + 8 * hf];
-          };
-          v8 a[N];
 #pragma unroll
-          for (int i = 0; i < kDqPF; ++i) a[i] = rd(i);
-#pragma unroll
-          for (int i = 0; i < N; ++i) {
-            if (i + kDqPF < N) a[i + kDqPF] = rd(i + kDqPF);
-            if (i & 1) dp = M::mma(a[i], gf[i / 2], dp);
-            else sv = M::mma(a[i], qf[i / 2], sv);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const v8 ak = *(const v8*)&kb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
+          const v8 av = *(const v8*)&vb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
+          sv = M::mma(ak, qf[ks], sv);
+          dp = M::mma(av, gf[ks], dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], c, -l2));
