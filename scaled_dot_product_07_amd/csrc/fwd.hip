@@ -168,7 +168,7 @@ fwd16_kernel(FwdParams p) {
 
   // ---- work unit: two query tiles of one (b|sequence, h)
   const int nbh = p.b * p.h;
-  const int pair = (int)(blockIdx.x / nbh);
+  int pair = (int)(blockIdx.x / nbh);
   const int bh = blockIdx.x % nbh;
   const int bi = bh / p.h, hi = bh % p.h;
   const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
@@ -214,7 +214,19 @@ fwd16_kernel(FwdParams p) {
   // the two tiles: causal without a left bound pairs (n-1-i, i), others
   // (2i, 2i+1); a missing tile (odd count) is -1
   const bool heavy_pair = CAUSAL && p.window_left < 0;
-  const int qt_a = heavy_pair ? p.n_qtiles - 1 - pair : 2 * pair;
+  // Packed sequences pair the tiles of each sequence among themselves (its
+  // own tile count n_qt; units past its (n_qt + 1) / 2 pairs are empty), and
+  // take the pair indices from the top: only the longest sequences have the
+  // high ones, so their units, the longest, start first.
+  int n_qt = p.n_qtiles;
+  if constexpr (VARLEN) {
+    if (heavy_pair) {
+      n_qt = (q_len + BM - 1) / BM;
+      pair = (p.n_qtiles + 1) / 2 - 1 - pair;
+    }
+  }
+  int qt_a = heavy_pair ? n_qt - 1 - pair : 2 * pair;
+  if (VARLEN && heavy_pair && pair >= (n_qt + 1) / 2) qt_a = -1;
   const int qt_b0 = heavy_pair ? pair : 2 * pair + 1;
   const int qt_b = (heavy_pair ? qt_b0 < qt_a : qt_b0 < p.n_qtiles) ? qt_b0 : -1;
   // keys a tile's rows see: [lo, hi) (empty when the tile has no rows)
