@@ -58,6 +58,21 @@ def test_small_vs_oracle(gpu, case):
     _check_all(inp, o, lse, 1 / np.sqrt(d), causal, dt)
 
 
+@pytest.mark.parametrize("case", [("bf16", 64), ("fp16", 128)], ids=lambda c: "-".join(map(str, c)))
+def test_causal_pairs_within_each_sequence(gpu, case):
+    """Causal units pair the query tiles of each sequence among themselves
+    (tile n_s-1-i with tile i of the sequence's own n_s tiles) and take the
+    longest sequences' pair indices first: every tile count from 0 to 9,
+    odd and even, in one pack, so that every pair slot is either a real
+    pair, a lone middle tile or empty for some sequence."""
+    dt, d = case
+    lens = [1100, 0, 129, 700, 385, 1, 900, 256, 1024, 640, 513, 128, 64, 300, 830]
+    announce(f"varlen causal tile pairs {case} lens={lens}")
+    inp = W.varlen_inputs(lens, lens, 2, d, dt, seed=410 + d)
+    o, lse = _run(inp, 2, d, 1 / np.sqrt(d), True, gpu)
+    _check_all(inp, o, lse, 1 / np.sqrt(d), True, dt)
+
+
 def test_unequal_q_kv_lengths_and_dead_rows(gpu):
     """Query and key lengths differ per sequence; a sequence with no keys gives dead rows."""
     lens_q = [40, 3, 129, 0, 70]
