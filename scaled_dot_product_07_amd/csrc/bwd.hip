@@ -136,10 +136,44 @@ __global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float
   }
 }
 
+// The dK/dV pass's Q and dO tiles in LDS: rows of D elements, unpadded,
+// whose 16-byte chunks are permuted by an XOR of the row index (only r mod
+// 16 matters), so that both ways a tile is read hit distinct banks: the MFMA
+// row-operand reads (ds_read_b128, 16 rows per phase) and the transposing
+// reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes). No row padding
+// serves both: the first needs a row stride of an odd number of 16-byte
+// groups modulo 256 B, the second one of 64 B. Logical chunk c of row r
+// sits at chunk c ^ tile_swz<D>(r).
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
+}
+
+// Row-operand read: row r, logical chunk ch (8 elements), with s = tile_swz(r).
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma16<T>::v8 read_row(const T* base, int r, int ch, int s) {
+  return *(const typename Mfma16<T>::v8*)&base[r * D + ((ch ^ s) << 3)];
+}
+
 // Transposing LDS read of an A operand: lane (16-group g, index i) receives
-// rows rbase + 4hf + 0..3 and + 8 .. 11 of column cbase + 16(g%2) + i.
+// rows rbase + 4hf + 0..3 and + 8 .. 11 of column cbase + 16(g%2) + i
+// (row = rbase + 4hf + (i / 4); s0, s1: tile_swz of row and of row + 8).
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row, int colv, int s0,
+                                                          int s1) {
+  const T* a0 = base + row * D + (((colv >> 3) ^ s0) << 3) + (colv & 7);
+  const T* a1 = base + (row + 8) * D + (((colv >> 3) ^ s1) << 3) + (colv & 7);
+  const i16x4 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a1));
+  return __builtin_bit_cast(typename Mfma16<T>::v8,
+                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The same read from a tile of padded rows (PITCH elements, no permutation).
 template <typename T, int PITCH>
-__device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row, int colv) {
+__device__ __forceinline__ typename Mfma16<T>::v8 read_tr_padded(const T* base, int row, int colv) {
   const T* a0 = base + row * PITCH + colv;
   const i16x4 lo =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
@@ -182,19 +216,22 @@ __device__ __forceinline__ void pack_b1(const f32x16& x, typename Mfma16<T>::v8 
 }
 
 // Loads one tile of `ROWS` rows x D of a (rows, d) tensor whose row r is at
-// base + r * stride, rows at or past `rows` reading as zeros.
-template <typename T, int D, int ROWS, int NT>
+// base + r * stride, rows at or past `rows` reading as zeros. In LDS the
+// tile's rows are either permuted (SWZ: D elements, chunk c of row r at
+// c ^ tile_swz(r)) or padded (D + 8 elements, chunks in order).
+template <typename T, int D, int ROWS, int NT, bool SWZ>
 struct TileLoader {
   static constexpr int CH = D / 8;
   static constexpr int CPT = ROWS * CH / NT;
   int roff[CPT], lrow[CPT], lofs[CPT];
-  __device__ void init(int tid, int64_t stride, int pitch) {
+  __device__ void init(int tid, int64_t stride) {
 #pragma unroll
     for (int x = 0; x < CPT; ++x) {
       const int ch = tid + NT * x;
       lrow[x] = ch / CH;
       roff[x] = lrow[x] * (int)stride * (int)sizeof(T) + (ch % CH) * 16;
-      lofs[x] = lrow[x] * pitch + (ch % CH) * 8;
+      lofs[x] = SWZ ? lrow[x] * D + (((ch % CH) ^ tile_swz<D>(lrow[x])) << 3)
+                    : lrow[x] * (D + 8) + (ch % CH) * 8;
     }
   }
   __device__ void load(i16x8 (&reg)[CPT], const T* tile_base, int rows) const {
@@ -230,12 +267,12 @@ struct TileLoader {
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(BwdParams p, const float* lse2) {
-  constexpr int BQ = kDkdvQ, PITCH = D + 8;
+  constexpr int BQ = kDkdvQ;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  using LQ = TileLoader<T, D, BQ, kDkdvThreads>;
-  __shared__ __attribute__((aligned(16))) T ql[3][BQ * PITCH];
-  __shared__ __attribute__((aligned(16))) T gl[2][BQ * PITCH];
+  using LQ = TileLoader<T, D, BQ, kDkdvThreads, true>;
+  __shared__ __attribute__((aligned(16))) T ql[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) T gl[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float l2l[2][BQ];
   __shared__ __attribute__((aligned(16))) float dll[2][BQ];
   // P of each pair and tile parity: [query block][register quad][lane][4]
@@ -290,8 +327,8 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   // iteration it covers query head hk * group + it / nt, tile t_lo + it % nt
   const int n_it = group * nt;
   LQ lq, lg;
-  lq.init(tid, p.q_ss, PITCH);
-  lg.init(tid, p.do_ss, PITCH);
+  lq.init(tid, p.q_ss);
+  lg.init(tid, p.do_ss);
   i16x8 qr[LQ::CPT], gr[LQ::CPT];
   float l2r = 0.f, dlr = 0.f;
   auto gload = [&](int it) {
@@ -323,6 +360,9 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   };
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+  // chunk permutations of the rows this lane reads (rows 32qb + col and
+  // 16t + vrow (+ 8) share those of col and vrow)
+  const int sr = tile_swz<D>(col % 16), st0 = tile_swz<D>(vrow), st1 = tile_swz<D>(vrow + 8);
   // acc += A2^T X over the 64 queries of a tile, A2^T read through the
   // transposing LDS read (dO^T for dV, Q^T for dK)
   auto accumulate = [&](const T* a2, const f32x16 (&x)[2]) {
@@ -332,7 +372,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const v8 a = read_tr<T, PITCH>(a2, 16 * t4 + vrow, 32 * db + vcol);
+        const v8 a = read_tr<T, D>(a2, 16 * t4 + vrow, 32 * db + vcol, st0, st1);
         acc[db] = M::mma(a, xb[t4], acc[db]);
       }
   };
@@ -345,7 +385,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       x[qb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const v8 a = *(const v8*)&a1[(32 * qb + col) * PITCH + 16 * ks + 8 * hf];
+        const v8 a = read_row<T, D>(a1, 32 * qb + col, 2 * ks + hf, sr);
         x[qb] = M::mma(a, bf[ks], x[qb]);
       }
     }
@@ -475,10 +515,12 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdParams p, const float* lse2) {
+  // K and V tiles in padded rows: the permuted layout's per-chunk address
+  // registers do not fit this kernel's register budget at d = 128
   constexpr int BK = kDqK, PITCH = D + 8;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  using LK = TileLoader<T, D, BK, kBwdThreads>;
+  using LK = TileLoader<T, D, BK, kBwdThreads, false>;
   __shared__ __attribute__((aligned(16))) T kl[2][BK * PITCH];
   __shared__ __attribute__((aligned(16))) T vl[2][BK * PITCH];
 
@@ -535,8 +577,8 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
       row0 >= sq.q_len ? 0 : (CAUSAL ? min(sq.kv_len, w_last + shift + 1) : sq.kv_len);
   const int wave_kv_begin = row0 + shift - window;
   LK lk, lv;
-  lk.init(tid, p.k_ss, PITCH);
-  lv.init(tid, p.v_ss, PITCH);
+  lk.init(tid, p.k_ss);
+  lv.init(tid, p.v_ss);
   i16x8 kr[LK::CPT], vr[LK::CPT];
   auto gload = [&](int j) {
     lk.load(kr, K + (int64_t)j * BK * p.k_ss, sq.kv_len - j * BK);
@@ -606,7 +648,7 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const v8 ak = read_tr<T, PITCH>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol);
+            const v8 ak = read_tr_padded<T, PITCH>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol);
             dq[db] = M::mma(ak, sb[t], dq[db]);
           }
       }
