@@ -89,11 +89,25 @@ template <typename TO, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 fwd8_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
-  constexpr int PITCH = D + 16;                   // bytes per LDS row (conflict-free reads)
   constexpr int CH = D / 16;                      // 16-byte chunks per row
+  // K and V tiles in LDS: rows of D bytes, unpadded, whose 16-byte chunks
+  // are permuted by an XOR of the row index (only r mod 16 matters; logical
+  // chunk c of row r sits at c ^ swz(r)), so that the K reads (16 rows x one
+  // chunk per ds_read_b128 phase), the V reads (rows {0..3, 8..11} + 4hf x
+  // two chunks per 32-lane ds_read_b64_tr_b8 phase) and the tile stores all
+  // hit distinct banks. No row padding serves the V reads: rows r and r + 8
+  // of a phase would always share banks.
+  auto swz = [](int r) -> int {
+    if constexpr (D <= 64) {
+      return (r >> 2) & 3;
+    } else {
+      const int k = (r >> 1) & 7;
+      return 4 * (k & 1) + 2 * ((k >> 2) & 1) + ((k >> 1) & 1);
+    }
+  };
   constexpr int CPT = BN * CH / kF8Threads;       // chunks per thread per tile
   static_assert(CPT >= 1 && BN * CH % kF8Threads == 0, "tile does not split over the threads");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][BN * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][BN * D];
 
   const Unit w = decode_unit<VARLEN>(p);
   if (w.qt * BM >= w.q_len) return;
@@ -160,8 +174,10 @@ fwd8_kernel(FwdParams p) {
   // addresses the row of key 32(j/2) + 16(j%2) + 8(e/4) + 4h + e%4 (e =
   // (m % 16) / 2, h = m / 32) at byte 32 db + 16 ((m / 16) % 2) + 8 (m % 2)
   const int te = (lane % 16) / 2;
-  const int v_lane_off =
-      (8 * (te / 4) + 4 * hf + te % 4) * PITCH + 16 * ((lane / 16) % 2) + 8 * (lane % 2);
+  const int v_row = 8 * (te / 4) + 4 * hf + te % 4;
+  const int v_lane_off = v_row * D + 8 * (lane % 2);
+  const int v_chunk = (lane / 16) % 2, v_swz = swz(v_row);
+  const int k_swz = swz(col);  // rows 32mb + col
 
   i32x4 kreg[CPT], vreg[CPT];
   auto load_tile = [&](int j) {
@@ -184,8 +200,9 @@ fwd8_kernel(FwdParams p) {
     for (int x = 0; x < CPT; ++x) {
       const int ch = tid + kF8Threads * x;
       const int r = ch / CH, cc = ch % CH;
-      *(i32x4*)&lds[buf][0][r * PITCH + cc * 16] = kreg[x];
-      *(i32x4*)&lds[buf][1][r * PITCH + cc * 16] = vreg[x];
+      const int at = r * D + ((cc ^ swz(r)) << 4);
+      *(i32x4*)&lds[buf][0][at] = kreg[x];
+      *(i32x4*)&lds[buf][1][at] = vreg[x];
     }
   };
 
@@ -209,8 +226,10 @@ fwd8_kernel(FwdParams p) {
         s[mb] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 64; ++kk) {
-          const unsigned char* kp = kl + (32 * mb + col) * PITCH + 64 * kk + 32 * hf;
-          const i32x4 lo = *(const i32x4*)kp, hi = *(const i32x4*)(kp + 16);
+          const unsigned char* kr = kl + (32 * mb + col) * D;
+          const int c0 = 4 * kk + 2 * hf;  // logical chunks c0, c0 + 1
+          const i32x4 lo = *(const i32x4*)(kr + ((c0 ^ k_swz) << 4));
+          const i32x4 hi = *(const i32x4*)(kr + (((c0 + 1) ^ k_swz) << 4));
           const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           s[mb] = mfma8(a, qf[kk], s[mb]);
         }
@@ -253,11 +272,12 @@ fwd8_kernel(FwdParams p) {
       // O^T += V^T P^T; l += rowsum(P) (row 0 of the ones product)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const unsigned char* vp = vl + v_lane_off + 32 * db;
+        // rows v_row + 16i keep v_row's permutation
+        const unsigned char* vp = vl + v_lane_off + (((2 * db + v_chunk) ^ v_swz) << 4);
         const i32x2 r0 = read_tr8(vp);
-        const i32x2 r1 = read_tr8(vp + 16 * PITCH);
-        const i32x2 r2 = read_tr8(vp + 32 * PITCH);
-        const i32x2 r3 = read_tr8(vp + 48 * PITCH);
+        const i32x2 r1 = read_tr8(vp + 16 * D);
+        const i32x2 r2 = read_tr8(vp + 32 * D);
+        const i32x2 r3 = read_tr8(vp + 48 * D);
         const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
         acc[db] = mfma8(a, pb, acc[db]);
       }
