@@ -191,8 +191,14 @@ sdpa_status sdpa_fwd_fp8_varlen(const void* q, const void* k, const void* v, voi
 /*
  * Bytes of device workspace the backward needs for these sizes: two fp32
  * values per query row (rowsum(dO * O) and the statistic in base 2), rounded
- * up to 256 bytes. The caller allocates it (256-byte aligned). For the packed
- * backward pass b = 1, s_q = total_q.
+ * up to 256 bytes. The caller allocates it (256-byte aligned) and passes it to
+ * sdpa_bwd*, so the library itself never allocates. For the packed backward
+ * pass b = 1, s_q = total_q. Returns 256 for empty problems; never fails.
+ * Cited: the cuDNN Graph API article, section 5: the caller sizes and
+ * allocates the device workspace of the built attention operation (its
+ * workspace_for / get_workspace_size step) and hands it to every execute
+ * call; cudnn-frontend PR #554's merge log (the SM80 backward entry) names
+ * the dO.O row dot product that this workspace holds.
  */
 size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype);
 
@@ -269,7 +275,15 @@ sdpa_status sdpa_bwd_varlen(const void* q, const void* k, const void* v, const v
                             const int64_t dv_stride[3], float scale, int causal,
                             int bottom_right, int window_left, void* stream);
 
-/* Message for the calling thread's last non-OK status ("" if none). */
+/*
+ * Message for the calling thread's last non-OK status ("" after a call that
+ * returned SDPA_OK). The string is owned by the library, stays valid until
+ * the calling thread's next sdpa_* call, and is never NULL.
+ * Cited: TransformerEngine PR #2964 "Refactor nvte_get_fused_attn_backend
+ * with cudnn-frontend calls": the support probe reports the backend's own
+ * error message as a string (empty when supported) instead of a bare
+ * "no backend" answer.
+ */
 const char* sdpa_last_error(void);
 
 /* Library version string. */

@@ -26,7 +26,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.cpp (the sanitizer test uses it)
+_LIB = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 

@@ -37,7 +37,9 @@ __all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_fp8_varlen", "bwd", "bwd_varlen"
            "library_path", "SdpaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsdpa07.so")
+# SDPA07_LIBRARY names another build of the library (e.g. one whose host code
+# carries sanitizers); by default the in-tree build next to this file
+_LIB_PATH = os.environ.get("SDPA07_LIBRARY") or os.path.join(_HERE, "libsdpa07.so")
 
 SDPA_OK, SDPA_ERR_INVALID_ARG, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH = 0, 1, 2, 3
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -133,6 +135,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPE_CODE[t.dtype]
 
 
+def _on_one_gpu(**named) -> None:
+    """Every tensor argument (None skipped) must live on one and the same GPU:
+    the library dereferences all of them on the device."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (found it on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _shape_like(name: str, t: Optional[torch.Tensor], ref: torch.Tensor) -> None:
+    if t is not None and tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+
+
 def _same_dtype(*ts):
     dt = ts[0].dtype
     for t in ts[1:]:
@@ -158,6 +182,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
     h_kv, s_kv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _on_one_gpu(q=q, k=k, v=v, out=out, lse=lse)
+    _shape_like("out", out, q)
     _same_dtype(q, k, v, out)
     if out is None:
         out = torch.empty_like(q)
@@ -199,6 +225,9 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     t_kv, h_kv = k.shape[0], k.shape[1]
     if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch between q, k, v")
+    _on_one_gpu(q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv, out=out,
+                lse=lse)
+    _shape_like("out", out, q)
     _same_dtype(q, k, v, out)
     total_q = t_q if total_q is None else int(total_q)
     total_kv = t_kv if total_kv is None else int(total_kv)
@@ -246,6 +275,10 @@ def bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = 
         raise ValueError("k/v shape mismatch")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, h, s_q):
         raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
+    _on_one_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    _shape_like("dq", dq, q)
+    _shape_like("dk", dk, k)
+    _shape_like("dv", dv, v)
     _same_dtype(q, k, v, o, dout, dq, dk, dv)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -291,6 +324,11 @@ def bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q: torch.Tensor, cu_seqlens_kv:
         raise ValueError("shape mismatch between q, k, v")
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
         raise ValueError("o and dout must have q's shape")
+    _on_one_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, cu_seqlens_q=cu_seqlens_q,
+                cu_seqlens_kv=cu_seqlens_kv, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    _shape_like("dq", dq, q)
+    _shape_like("dk", dk, k)
+    _shape_like("dv", dv, v)
     _same_dtype(q, k, v, o, dout, dq, dk, dv)
     total_q = t_q if total_q is None else int(total_q)
     total_kv = t_kv if total_kv is None else int(total_kv)
@@ -358,6 +396,8 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     h_kv, s_kv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _on_one_gpu(q=q, k=k, v=v, out=out, lse=lse, descale_q=descale_q, descale_k=descale_k,
+                descale_v=descale_v, scale_o=scale_o, amax_o=amax_o)
     extras = _fp8_common(q, k, v, out_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)
     if out is None:
         out = torch.empty(q.shape, device=q.device, dtype=out_dtype)
@@ -402,6 +442,9 @@ def fwd_fp8_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
     t_kv, h_kv = k.shape[0], k.shape[1]
     if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch between q, k, v")
+    _on_one_gpu(q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv, out=out,
+                lse=lse, descale_q=descale_q, descale_k=descale_k, descale_v=descale_v,
+                scale_o=scale_o, amax_o=amax_o)
     extras = _fp8_common(q, k, v, out_dtype, descale_q, descale_k, descale_v, scale_o, amax_o)
     total_q = t_q if total_q is None else int(total_q)
     total_kv = t_kv if total_kv is None else int(total_kv)

@@ -703,7 +703,6 @@ template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
   BwdParams arg = p;
   const long long n = VARLEN ? (long long)p.total_q * p.h : (long long)p.b * p.h * p.s_q;
-  float* lse2 = p.delta + (n + 63) / 64 * 64;
   hipError_t e;
   if (!VARLEN && (p.s_q == 0 || p.s_kv == 0)) {
     // nothing to recompute: every gradient is zero
@@ -719,6 +718,26 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
                              stream);
     return hipSuccess;
   }
+  if (VARLEN && (p.total_q == 0 || p.total_kv == 0)) {
+    // a packed batch with no keys (or no queries) anywhere: every gradient row
+    // is zero, and O, dO, the statistic and the workspace are neither needed
+    // nor read (the entry point does not require them in this case)
+    int one = 1;
+    int64_t no_sb = 0;
+    if (p.total_kv > 0) {
+      int rows = p.total_kv;
+      e = zero_rows<T, D>(arg.dk, no_sb, arg.dk_sh, arg.dk_ss, one, arg.h_kv, rows, stream);
+      if (e != hipSuccess) return e;
+      return zero_rows<T, D>(arg.dv, no_sb, arg.dv_sh, arg.dv_ss, one, arg.h_kv, rows, stream);
+    }
+    if (p.total_q > 0) {
+      int rows = p.total_q;
+      return zero_rows<T, D>(arg.dq, no_sb, arg.dq_sh, arg.dq_ss, one, arg.h, rows, stream);
+    }
+    return hipSuccess;
+  }
+  // the workspace: D for every query row (padded to 64), then LSE in base 2
+  float* lse2 = p.delta + (n + 63) / 64 * 64;
   if (n > 0) {
     const int rpb = kPreThreads / (D / 8);
     void* args[] = {&arg, &lse2, (void*)&n};

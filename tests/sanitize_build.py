@@ -1,0 +1,51 @@
+"""Host-side sanitizer builds for the CPU tests (ASan + UBSan, g++).
+
+Builds, into a directory given on the command line (or by build()):
+  liboracle_san.so  oracle/oracle.cpp with -fsanitize=address,undefined;
+  libsdpa07_san.so  the library with its host layer (csrc/abi.cpp: argument
+                    validation and dispatch) compiled with the same sanitizers
+                    by g++, linked with the device objects of the last regular
+                    build (_build/, made by scaled_dot_product_07_amd.build);
+                    the device code itself is not instrumented.
+Only the CPU sanitizer test runs this; nothing on a GPU loads these builds.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SAN = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+DEVICE_OBJECTS = ("fwd", "fwd_fp8", "bwd")
+
+
+def build(out_dir: str) -> dict:
+    os.makedirs(out_dir, exist_ok=True)
+    oracle_so = os.path.join(out_dir, "liboracle_san.so")
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-pthread",
+                    "-fno-fast-math", "-ffp-contract=off", *SAN,
+                    os.path.join(ROOT, "oracle", "oracle.cpp"), "-o", oracle_so], check=True)
+    abi_o = os.path.join(out_dir, "abi_san.o")
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), *SAN, "-c",
+                    os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", "abi.cpp"), "-o",
+                    abi_o], check=True)
+    objs = []
+    for name in DEVICE_OBJECTS:
+        src = os.path.join(ROOT, "_build", f"{name}.hip.o")
+        if not os.path.exists(src):
+            raise FileNotFoundError(f"{src}: run the regular build first")
+        dst = os.path.join(out_dir, f"{name}_dev.o")
+        shutil.copyfile(src, dst)
+        objs.append(dst)
+    lib_so = os.path.join(out_dir, "libsdpa07_san.so")
+    subprocess.run(["g++", "-shared", "-fPIC", *SAN, abi_o, *objs, "-L/opt/rocm/lib",
+                    "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", lib_so], check=True)
+    return {"oracle": oracle_so, "lib": lib_so}
+
+
+if __name__ == "__main__":
+    print(build(sys.argv[1] if len(sys.argv) > 1 else os.path.join(ROOT, "_build", "san")))

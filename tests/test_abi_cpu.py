@@ -336,3 +336,59 @@ def test_python_binding_maps_statuses(lib):
         sdpa._check(UNSUPPORTED)
     with pytest.raises(ValueError):
         sdpa._check(INVALID)
+
+
+# ---- the Python binding rejects bad tensor arguments before any launch -------
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def _binding_calls():
+    import torch
+    q, k = _cpu(1, 2, 8, 64), _cpu(1, 2, 8, 64)
+    lse = _cpu(1, 2, 8, dtype=torch.float32)
+    tq = _cpu(8, 2, 64)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    tl = _cpu(8, 2, dtype=torch.float32)
+    f8 = torch.zeros(1, 2, 8, 64, dtype=torch.float8_e4m3fn)
+    t8 = torch.zeros(8, 2, 64, dtype=torch.float8_e4m3fn)
+    return {
+        "fwd": lambda s: s.fwd(q, k, k),
+        "fwd_varlen": lambda s: s.fwd_varlen(tq, tq, tq, cu, cu, 8, 8),
+        "bwd": lambda s: s.bwd(q, k, k, q, q, lse),
+        "bwd_varlen": lambda s: s.bwd_varlen(tq, tq, tq, tq, tq, tl, cu, cu, 8, 8),
+        "fwd_fp8": lambda s: s.fwd_fp8(f8, f8, f8),
+        "fwd_fp8_varlen": lambda s: s.fwd_fp8_varlen(t8, t8, t8, cu, cu, 8, 8),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_binding_calls()))
+def test_binding_rejects_host_tensors(lib, name):
+    """Host (CPU) tensors would be dereferenced as device addresses: refused."""
+    import scaled_dot_product_07_amd as sdpa
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _binding_calls()[name](sdpa)
+
+
+def test_binding_shape_checks():
+    import scaled_dot_product_07_amd as sdpa
+    q = _cpu(1, 2, 8, 64)
+    sdpa._shape_like("out", None, q)
+    sdpa._shape_like("out", _cpu(1, 2, 8, 64), q)
+    with pytest.raises(ValueError, match="out has shape"):
+        sdpa._shape_like("out", _cpu(1, 2, 7, 64), q)
+    with pytest.raises(ValueError, match="must be a torch.Tensor"):
+        sdpa._on_one_gpu(q=3)
+
+
+def test_bwd_varlen_without_keys_needs_no_forward_outputs(lib):
+    """A packed batch with no keys: O, dO, the statistic and the workspace are
+    not read, so NULL passes validation (the kernels only zero dQ); on a host
+    without a GPU the launch itself then fails with SDPA_ERR_LAUNCH."""
+    s = S3(2 * 64, 64, 1)
+    st = lib.sdpa_bwd_varlen(ALIGNED, None, None, None, None, None, ALIGNED, None, None, ALIGNED,
+                             ALIGNED, 2, 16, 0, 9, 0, None, 0, BF16, 2, 2, 64, s, s, s, s, s, s, s,
+                             s, 0.1, 1, 0, -1, None)
+    assert st in (OK, 3), lib.sdpa_last_error()

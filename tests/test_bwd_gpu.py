@@ -102,21 +102,43 @@ def test_empty_sides_give_zero_gradients(gpu):
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
 
 
-def test_workload_bwd_b4h16s2048d128_sampled(gpu):
-    """The backward workload at full size: two whole heads against the oracle,
-    plus identities on every head: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0."""
+def test_workload_bwd_b4h16s2048d128_full(gpu):
+    """The backward workload at full size, in the benchmark's launch
+    configuration (O and LSE from the GPU forward): every element of dQ, dK, dV
+    of all 64 heads against the oracle, plus the identities
+    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 on every head."""
     c = W.BWD_BF16_B4H16S2048D128
     announce(c.name)
     q, k, v, do = W.case_inputs(c)
     dq, dk, dv = _gpu_bwd(q, k, v, do, c.scale, True, gpu)
-    for (bi, hi) in [(0, 0), (3, 15)]:
-        sl = lambda x: f64(x[bi:bi + 1, hi:hi + 1])  # noqa: E731
-        _, _, dq_r, dk_r, dv_r = oracle.bwd(sl(q), sl(k), sl(v), sl(do), c.scale, True)
-        check_grad(sl(dq), dq_r, f"dQ[b{bi},h{hi}]")
-        check_grad(sl(dk), dk_r, f"dK[b{bi},h{hi}]")
-        check_grad(sl(dv), dv_r, f"dV[b{bi},h{hi}]")
+    _, _, dq_r, dk_r, dv_r = oracle.bwd(f64(q), f64(k), f64(v), f64(do), c.scale, True)
+    check_grad(f64(dq), dq_r, "dQ")
+    check_grad(f64(dk), dk_r, "dK")
+    check_grad(f64(dv), dv_r, "dV")
     dv_sum = dv.double().sum(2)
     do_sum = do.to(gpu).double().sum(2)
     assert torch.max(torch.abs(dv_sum - do_sum)) <= 5e-2 * torch.max(torch.abs(do_sum))
     dk_sum = dk.double().sum(2)
     assert torch.max(torch.abs(dk_sum)) <= 5e-2 * torch.max(torch.abs(dk.double()))
+
+
+def test_guard_bands_untouched(gpu):
+    """Nothing is written outside dQ, dK, dV: canaries after each survive
+    (dense, causal, ragged tiles)."""
+    import scaled_dot_product_07_amd as sdpa
+    announce("bwd guard bands")
+    b, h, s, d = 1, 2, 200, 64
+    q, k, v, do = (x.to(gpu) for x in W.dense_inputs(b, h, s, s, d, "bf16", "bhsd", seed=27,
+                                                     with_dout=True))
+    o, lse = sdpa.fwd(q, k, v, causal=True)
+    n = b * h * s * d
+    bufs = [torch.full((n + 4096,), 123.0, dtype=torch.bfloat16, device=gpu) for _ in range(3)]
+    dq, dk, dv = (x[:n].view(b, h, s, d) for x in bufs)
+    ws_n = sdpa.bwd_workspace_size(b, h, s, d, torch.bfloat16)
+    wbuf = torch.full((ws_n + 1024,), 7, dtype=torch.uint8, device=gpu)
+    sdpa.bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=wbuf[:ws_n])
+    torch.cuda.synchronize()
+    for x in bufs:
+        assert torch.all(x[n:] == 123.0)
+    assert torch.all(wbuf[ws_n:] == 7)
+    assert torch.all(torch.isfinite(dq.float())) and torch.any(dq != 123.0)

@@ -235,3 +235,28 @@ def test_varlen_workload_sampled(gpu):
             check_grad(sl(dq), dq_r, f"dQ[seq{si},h{hi}]")
             check_grad(sl(dk), dk_r, f"dK[seq{si},h{hi}]")
             check_grad(sl(dv), dv_r, f"dV[seq{si},h{hi}]")
+
+
+def test_varlen_without_keys_reads_no_forward_outputs(gpu):
+    """A packed batch whose sequences have no keys at all: every dQ row is zero
+    and O, dO, the statistic and the workspace may be NULL (they are not read)."""
+    import ctypes
+    import scaled_dot_product_07_amd as sdpa
+    announce("bwd varlen total_kv=0 with NULL forward outputs")
+    lib = sdpa._load()
+    lens = [40, 3, 0, 90]
+    tq, h, d = sum(lens), 2, 64
+    cu_q = W.cu_seqlens(lens).to(gpu)
+    cu_kv = torch.zeros(len(lens) + 1, dtype=torch.int32, device=gpu)
+    q = torch.randn(tq, h, d, dtype=torch.bfloat16, device=gpu)
+    dq = torch.full_like(q, 9.0)
+    st3 = lambda t: (ctypes.c_int64 * 3)(*t.stride())  # noqa: E731
+    z3 = (ctypes.c_int64 * 3)(h * d, d, 1)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = lib.sdpa_bwd_varlen(p(q), None, None, None, None, None, p(dq), None, None, p(cu_q),
+                             p(cu_kv), len(lens), tq, 0, max(lens), 0, None, 0, 2, h, h, d,
+                             st3(q), z3, z3, z3, z3, st3(dq), z3, z3, 0.125, 1, 0, -1,
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, sdpa.last_error()
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)

@@ -4,8 +4,8 @@ Small cases run the whole oracle (several 128-row query tiles and 64-key
 tiles, ragged tails, both dtypes of 16 bits, fp32, both head dims, causal and
 not, rectangular s_q != s_kv, BSHD strides, negative and zero scale, no keys).
 The workloads at full size run in the same launch configuration as the
-benchmark and are checked on whole heads (the oracle runs them in seconds) or
-on sampled query rows of sampled heads.
+benchmark and are checked element by element against the oracle over their
+whole outputs.
 """
 
 import numpy as np
@@ -188,24 +188,15 @@ def test_workload_bf16_b4h16s1024d64_full(gpu):
     check_lse(f64(lse), lse_ref)
 
 
-def _sampled_rows_check(q, k, v, o, lse, scale, causal, dt, heads, rows):
-    q64, k64, v64 = f64(q), f64(k), f64(v)
-    o64, l64 = f64(o), f64(lse)
-    for (bi, hi) in heads:
-        o_ref, lse_ref = oracle.attn_rows(q64[bi, hi, rows], rows, k64[bi, hi], v64[bi, hi],
-                                          scale, causal)
-        check_o(o64[bi, hi, rows], o_ref, dt, what=f"O[b{bi},h{hi}]")
-        check_lse(l64[bi, hi, rows], lse_ref, what=f"LSE[b{bi},h{hi}]")
-
-
 @pytest.mark.parametrize("case", [W.FWD_BF16_B2H16S4096D128, W.FWD_FP16_B2H16S4096D128],
                          ids=["bf16", "fp16"])
-def test_workload_b2h16s4096d128_bshd_sampled(gpu, case):
+def test_workload_b2h16s4096d128_bshd_full(gpu, case):
+    """The non-causal BSHD workload at full size, in the benchmark's launch
+    configuration: every output element and every statistic against the oracle."""
     announce(case.name)
     q, k, v = W.case_inputs(case)
     assert q.stride() == (4096 * 16 * 128, 128, 16 * 128, 1)  # BSHD viewed as BHSD
     o, lse = _run(q, k, v, case.scale, case.causal, gpu)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095], rng.integers(0, 4096, 120)]))
-    _sampled_rows_check(q, k, v, o, lse, case.scale, case.causal, case.dtype,
-                        [(0, 0), (1, 15), (0, 9)], rows)
+    o_ref, lse_ref = oracle.fwd(f64(q), f64(k), f64(v), case.scale, case.causal)
+    check_o(f64(o), o_ref, case.dtype)
+    check_lse(f64(lse), lse_ref)

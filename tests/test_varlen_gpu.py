@@ -93,8 +93,10 @@ def test_loose_max_seqlen_bound(gpu):
     _check_all(inp, o, lse, 0.1, True, "bf16")
 
 
-def test_workload_varlen_32seq_sampled(gpu):
-    """The packed workload at full size: 32 sequences, h16 d128, causal bf16."""
+def test_workload_varlen_32seq_full(gpu):
+    """The packed workload at full size (32 sequences, h16 d128, causal bf16) in
+    the benchmark's launch configuration: every row of every sequence and head
+    against the oracle, and the NaN-poisoned capacity tail never reaches O."""
     c = W.VARLEN_BF16_32SEQ_H16D128
     inp = W.varlen_case_inputs(c)
     announce(f"{c.name} T={inp.total_q}")
@@ -103,17 +105,7 @@ def test_workload_varlen_32seq_sampled(gpu):
     o64, l64 = f64(o[:tq]), f64(lse[:tq])
     assert np.all(np.isfinite(o64)), "NaN from the poisoned capacity tail reached O"
     assert torch.all(o[tq:] == 77.0) and torch.all(lse[tq:] == 55.0)
-    lens = inp.lens_q.numpy()
-    cu = inp.cu_q.numpy()
-    pick = sorted({0, len(lens) - 1, int(np.argmax(lens)), int(np.argmin(lens))})
-    rng = np.random.default_rng(9)
-    q64, k64, v64 = f64(inp.q[:tq]), f64(inp.k[:tq]), f64(inp.v[:tq])
-    for n in pick:
-        L = int(lens[n])
-        rows = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 24)]))
-        for hi in (0, 7, 15):
-            s0 = int(cu[n])
-            o_ref, l_ref = oracle.attn_rows(q64[s0 + rows, hi], rows, k64[s0:s0 + L, hi],
-                                            v64[s0:s0 + L, hi], c.scale, True)
-            check_o(o64[s0 + rows, hi], o_ref, "bf16", what=f"O[seq{n},h{hi}]")
-            check_lse(l64[s0 + rows, hi], l_ref, what=f"LSE[seq{n},h{hi}]")
+    o_ref, l_ref = oracle.fwd_varlen(f64(inp.q[:tq]), f64(inp.k[:tq]), f64(inp.v[:tq]),
+                                     inp.cu_q.numpy(), inp.cu_kv.numpy(), c.scale, True)
+    check_o(o64, o_ref, "bf16")
+    check_lse(l64, l_ref)
