@@ -6,14 +6,15 @@ A step is one launch of the forward over the headline workload: causal bf16
 attention at b4 h16 s1024 d64, BHSD, scale 1/8, inputs iid N(0,1) from a fixed
 seed, already resident in HBM. W untimed launches, then exactly K timed steps,
 each one a 512 MiB write (which evicts the L2 caches and the MALL) followed by
-the launch, timed with HIP events recorded around the launch on the launch
-stream (torch's current stream, which the binding launches on), bracketed by
-device synchronisation. `value` and `ms_per_step` are the MEDIAN of the K
-cold-cache launch times; `roofline.achieved` uses their MEAN (the figure the
-rocprofv3 kernel-trace average of the same command is compared with). The
-figures are tagged [hip-events]: they come from HIP events, not from a
-profiler. Warm-cache figures (back-to-back launches, caches holding the
-inputs) are reported separately, labelled, under `extra`.
+the launch, bracketed by device synchronisation. The device time of each
+launch comes from the kernel trace that torch's profiler collects through
+ROCm's tracer (the kernel's own begin and end); `value` and `ms_per_step` are
+the MEDIAN over the K steps and `roofline.achieved` uses the MEAN [kernel-trace].
+As a cross-check, HIP events on the launch stream time K x (flush + launch)
+and K x flush alone; their difference / K is reported as
+`roofline.events_mean_launch_ms` (and becomes the figure, tagged [hip-events],
+if the trace is unavailable). Warm-cache figures (back-to-back launches,
+caches holding the inputs) are reported separately, labelled, under `extra`.
 
 FLOP count: the pages' formula 4*b*h*s^2*d, halved when causal ("Inside
 NVIDIA's cuDNN Graph API ...", section 5). Roofline: MFMA-bound against the
@@ -152,27 +153,70 @@ def time_launches(fn, steps, warmup, torch, graph=True):
     return start.elapsed_time(stop) / steps
 
 
-def time_cold(fn, iters, torch, flush_bytes=512 << 20, flush=None):
-    """Cold-cache launch times (ms): before each launch `flush_bytes` are written,
-    which evicts the L2 caches and the MALL; HIP events are recorded right around
-    the launch on the current stream. Returns (median, mean, list)."""
-    buf = flush if flush is not None else torch.empty(flush_bytes, dtype=torch.uint8,
-                                                      device="cuda")
-    evs = []
+def _is_ours(name: str) -> bool:
+    """Kernels of this library (all live in namespace sdpa07)."""
+    return "sdpa07" in name
+
+
+def time_cold(fn, iters, torch, flush, trace=True):
+    """Cold-cache timing of `iters` calls, each preceded by writing the whole
+    `flush` buffer (512 MiB: evicts the L2 caches and the MALL).
+
+    Two measurements of the same kind of timed region:
+      trace   per-call device time of this library's kernels (summed over the
+              kernels of one call) from the kernel trace that torch's profiler
+              collects through ROCm's tracer: median and mean;
+      events  HIP events on the launch stream around `iters` x (flush + call)
+              and around `iters` x flush alone; their difference / iters is
+              the mean device time per call (launches queue back to back, so no
+              dispatch gap is counted; events around one launch would include
+              the launch latency).
+    Returns a dict of ms figures; the trace part is None when the profiler
+    yields no kernel records."""
+    out = {"trace_median_ms": None, "trace_mean_ms": None}
     torch.cuda.synchronize()
-    for i in range(iters):
-        buf.fill_(i & 0x7f)
+    try:
+        if not trace:
+            raise RuntimeError("kernel trace switched off (--no-trace)")
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(iters):
+                flush.fill_(i & 0x7f)
+                fn()
+            torch.cuda.synchronize()
+        per_call, cur, seen = [], 0.0, False
+        for e in sorted((e for e in prof.events() if e.device_type.name == "CUDA"),
+                        key=lambda e: e.time_range.start):
+            if _is_ours(e.name):
+                cur += (e.time_range.end - e.time_range.start) * 1e-3
+                seen = True
+            elif seen:
+                per_call.append(cur)
+                cur, seen = 0.0, False
+        if seen:
+            per_call.append(cur)
+        if len(per_call) == iters:
+            out["trace_median_ms"] = float(np.median(per_call))
+            out["trace_mean_ms"] = float(np.mean(per_call))
+    except Exception as ex:  # reported, never hidden
+        out["trace_error"] = repr(ex)[:200]
+
+    def region(with_call):
         a = torch.cuda.Event(enable_timing=True)
         z = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record()
-        fn()
+        for i in range(iters):
+            flush.fill_(i & 0x7f)
+            if with_call:
+                fn()
         z.record()
-        evs.append((a, z))
-    torch.cuda.synchronize()
-    ts = [a.elapsed_time(z) for a, z in evs]
-    if flush is None:
-        del buf
-    return float(np.median(ts)), float(np.mean(ts)), ts
+        torch.cuda.synchronize()
+        return a.elapsed_time(z)
+
+    t_both, t_flush = region(True), region(False)
+    out["events_mean_ms"] = (t_both - t_flush) / iters
+    return out
 
 
 def traffic_from_counters():
@@ -265,6 +309,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick-cpu-baseline", action="store_true",
                     help="time the oracle on the two small forward workloads only")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="time with HIP events only (when an outside profiler traces the run)")
     ap.add_argument("--warm", action="store_true",
                     help="time back-to-back launches without the cache flush (for counters)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -303,10 +349,18 @@ def main():
     if args.warm:
         ms = ms_mean = time_launches(step, args.steps, 0, torch, graph=False)
         timing = "warm: back-to-back launches, mean [hip-events]"
+        cold = None
     else:
-        ms, ms_mean, _ = time_cold(step, args.steps, torch, flush=flush)
-        timing = ("cold: 512 MiB written before each launch; median of the steps, "
-                  "roofline on their mean [hip-events]")
+        cold = time_cold(step, args.steps, torch, flush, trace=not args.no_trace)
+        if cold["trace_median_ms"] is not None:
+            ms, ms_mean = cold["trace_median_ms"], cold["trace_mean_ms"]
+            timing = ("cold: 512 MiB written before each launch; device time of the kernel from "
+                      "the kernel trace (torch profiler over ROCm's tracer): value = median, "
+                      "roofline = mean [kernel-trace]")
+        else:
+            ms = ms_mean = cold["events_mean_ms"]
+            timing = ("cold: 512 MiB written before each launch; mean device time from HIP events "
+                      "(K x (flush + launch) minus K x flush) [hip-events]")
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_mean = flops / (ms_mean * 1e-3) / 1e12
     traffic = traffic_from_counters()
@@ -331,6 +385,10 @@ def main():
                      "frac": round(tflops_mean / PEAK_BF16_TFLOPS, 4),
                      "mean_launch_ms": round(ms_mean, 6), "traffic": traffic},
     }
+    if cold is not None:
+        result["roofline"]["events_mean_launch_ms"] = round(cold["events_mean_ms"], 6)
+        if "trace_error" in cold:
+            result["roofline"]["trace_error"] = cold["trace_error"]
 
     extra = {}
     if not args.no_extra:
@@ -340,7 +398,7 @@ def main():
             "label": "warm cache (no flush), back-to-back launches [hip-events]",
             "graph_replay_ms": round(w_graph, 6), "eager_ms": round(w_eager, 6),
             "tflops_graph_replay": round(flops / (w_graph * 1e-3) / 1e12, 3)}
-        extra.update(bench_other_workloads(torch, sdpa, W, dev, flush))
+        extra.update(bench_other_workloads(torch, sdpa, W, dev, flush, not args.no_trace))
     del flush
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, quick=args.quick_cpu_baseline)
@@ -355,32 +413,36 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _both(fn, flops, torch, flush, cold_iters=20, warm_iters=50):
-    """Cold (flushed, median) and warm (back-to-back graph replay, mean) figures."""
+def _both(fn, flops, torch, flush, cold_iters=20, warm_iters=50, trace=True):
+    """Cold (flushed; kernel-trace median, else HIP-event mean) and warm
+    (back-to-back graph replay, HIP-event mean) figures."""
     for _ in range(3):
         fn()
-    cold, _, _ = time_cold(fn, cold_iters, torch, flush=flush)
+    c = time_cold(fn, cold_iters, torch, flush, trace=trace)
+    cold = c["trace_median_ms"] if c["trace_median_ms"] is not None else c["events_mean_ms"]
     warm = time_launches(fn, warm_iters, 3, torch, graph=True)
     tc = flops / (cold * 1e-3) / 1e12
     tw = flops / (warm * 1e-3) / 1e12
     return {"cold_ms": round(cold, 6), "tflops": round(tc, 3),
             "frac_of_mfma_peak": round(tc / PEAK_BF16_TFLOPS, 4),
+            "cold_events_mean_ms": round(c["events_mean_ms"], 6),
             "warm_ms": round(warm, 6), "warm_tflops": round(tw, 3)}
 
 
-def bench_other_workloads(torch, sdpa, W, dev, flush):
+def bench_other_workloads(torch, sdpa, W, dev, flush, trace=True):
     out = {}
+    both = lambda *a, **kw: _both(*a, trace=trace, **kw)  # noqa: E731
     # fp32 causal b1 h2 s128 d64 (latency-bound correctness workload)
     c = W.FWD_FP32_B1H2S128D64
     q, k, v = (x.to(dev) for x in W.case_inputs(c))
-    out["fwd_fp32_b1h2s128d64_causal"] = _both(
+    out["fwd_fp32_b1h2s128d64_causal"] = both(
         lambda: sdpa.fwd(q, k, v, scale=c.scale, causal=True), fwd_flops(1, 2, 128, 128, 64, True),
         torch, flush)
     # non-causal b2 h16 s4096 d128 BSHD, bf16 and fp16
     for c in (W.FWD_BF16_B2H16S4096D128, W.FWD_FP16_B2H16S4096D128):
         q, k, v = (x.to(dev) for x in W.case_inputs(c))
         o = torch.empty_like(q)
-        out[f"fwd_{c.dtype}_b2h16s4096d128_bshd"] = _both(
+        out[f"fwd_{c.dtype}_b2h16s4096d128_bshd"] = both(
             lambda: sdpa.fwd(q, k, v, scale=c.scale, causal=False, out=o),
             fwd_flops(c.b, c.h, c.s_q, c.s_kv, c.d, False), torch, flush)
         del q, k, v, o
@@ -394,7 +456,7 @@ def bench_other_workloads(torch, sdpa, W, dev, flush):
     lse = torch.empty(q.shape[0], c.h, device=dev, dtype=torch.float32)
     lens = inp.lens_q.double()
     vflops = float((4.0 * c.h * lens * lens * c.d * 0.5).sum())
-    e = _both(lambda: sdpa.fwd_varlen(q, k, v, cu, cu, mx, mx, total_q=inp.total_q,
+    e = both(lambda: sdpa.fwd_varlen(q, k, v, cu, cu, mx, mx, total_q=inp.total_q,
                                       total_kv=inp.total_kv, scale=c.scale, causal=True, out=o,
                                       lse=lse), vflops, torch, flush)
     e["total_tokens"] = inp.total_q
@@ -405,7 +467,7 @@ def bench_other_workloads(torch, sdpa, W, dev, flush):
     for c, layout in ((W.FWD_BF16_B4H16S1024D64, "causal"), (W.FWD_BF16_B2H16S4096D128, "bshd")):
         q, k, v = (x.to(dev).to(torch.float8_e4m3fn) for x in W.case_inputs(c))
         o = torch.empty(q.shape, device=dev, dtype=torch.bfloat16)
-        e = _both(lambda: sdpa.fwd_fp8(q, k, v, scale=c.scale, causal=c.causal, out=o,
+        e = both(lambda: sdpa.fwd_fp8(q, k, v, scale=c.scale, causal=c.causal, out=o,
                                        return_lse=False),
                   fwd_flops(c.b, c.h, c.s_q, c.s_kv, c.d, c.causal), torch, flush)
         e["frac_of_fp8_mfma_peak"] = round(e["tflops"] / PEAK_FP8_TFLOPS, 4)
@@ -418,7 +480,7 @@ def bench_other_workloads(torch, sdpa, W, dev, flush):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(sdpa.bwd_workspace_size(c.b, c.h, c.s_q, c.d, q.dtype),
                      dtype=torch.uint8, device=dev)
-    e = _both(lambda: sdpa.bwd(q, k, v, o, do, lse, scale=c.scale, causal=True, dq=dq, dk=dk,
+    e = both(lambda: sdpa.bwd(q, k, v, o, do, lse, scale=c.scale, causal=True, dq=dq, dk=dk,
                                dv=dv, workspace=ws),
               2.5 * fwd_flops(c.b, c.h, c.s_q, c.s_kv, c.d, True), torch, flush, cold_iters=10,
               warm_iters=20)
