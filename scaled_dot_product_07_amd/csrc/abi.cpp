@@ -18,7 +18,7 @@
 #include <cstdlib>
 #include <string>
 
-#include "../../include/sdpa.h"
+#include "sdpa.h"
 #include "sdpa_internal.h"
 
 namespace {

@@ -19,7 +19,6 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SAN = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
-DEVICE_OBJECTS = ("fwd", "fwd_fp8", "bwd")
 
 
 def build(out_dir: str) -> dict:
@@ -33,8 +32,10 @@ def build(out_dir: str) -> dict:
                     "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), *SAN, "-c",
                     os.path.join(ROOT, "scaled_dot_product_07_amd", "csrc", "abi.cpp"), "-o",
                     abi_o], check=True)
+    sys.path.insert(0, ROOT)
+    from scaled_dot_product_07_amd.build import SOURCES
     objs = []
-    for name in DEVICE_OBJECTS:
+    for name in (src[:-4] for src in SOURCES if src.endswith(".hip")):
         src = os.path.join(ROOT, "_build", f"{name}.hip.o")
         if not os.path.exists(src):
             raise FileNotFoundError(f"{src}: run the regular build first")
