@@ -248,6 +248,36 @@ sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void*
                         int window_left, void* stream);
 
 /*
+ * sdpa_bwd_ex without a workspace argument, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation. Arguments, results and errors are those of
+ * sdpa_bwd_ex; the caller still provides every input and output.
+ *   The workspace is a fixed array in the library's device code,
+ *   SDPA_BWD_FIXED_WORKSPACE_BYTES (16 MiB) on each device the library runs
+ *   on, held until the process ends. It serves b * h * s_q up to
+ *   SDPA_BWD_FIXED_WORKSPACE_ROWS (2^21) query rows; more is rejected with
+ *   SDPA_ERR_UNSUPPORTED before anything is launched.
+ *   Allocates nothing: no hipMalloc / hipFree. The first call on a device
+ *   (the current device, which `stream` must belong to) looks up the array's
+ *   device address once; failure there is SDPA_ERR_LAUNCH.
+ *   Every call on one device uses that device's one array: calls that
+ *   overlap on a device (other streams, other threads) race and must be
+ *   serialised by the caller. Each call writes every workspace value it
+ *   reads, so what an earlier call left there does not matter.
+ */
+#define SDPA_BWD_FIXED_WORKSPACE_BYTES (16u << 20)
+#define SDPA_BWD_FIXED_WORKSPACE_ROWS (1 << 21)
+sdpa_status sdpa_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                sdpa_dtype dtype, int b, int h, int h_kv, int s_q, int s_kv,
+                                int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                                const int64_t v_stride[4], const int64_t o_stride[4],
+                                const int64_t do_stride[4], const int64_t dq_stride[4],
+                                const int64_t dk_stride[4], const int64_t dv_stride[4],
+                                float scale, int causal, int bottom_right, int window_left,
+                                void* stream);
+
+/*
  * Packed THD backward (fp16/bf16), with grouped-query heads and the band
  * options as sdpa_bwd_ex.
  *   q, o, dout, dq: (total_q, h, d); k, v, dk, dv: (total_kv, h_kv, d); each

@@ -32,8 +32,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_fp8_varlen", "bwd", "bwd_varlen",
-           "bwd_workspace_size", "last_error", "version",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_fp8_varlen", "bwd", "bwd_noalloc",
+           "bwd_varlen", "bwd_workspace_size", "last_error", "version",
            "library_path", "SdpaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,10 +85,13 @@ def _load():
                              S4, S4, S4, S4, S4, S4, S4, S4, F, I, P]
     lib.sdpa_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I,
                                 S4, S4, S4, S4, S4, S4, S4, S4, F, I, I, I, P]
+    lib.sdpa_bwd_ex_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                        S4, S4, S4, S4, S4, S4, S4, S4, F, I, I, I, P]
     lib.sdpa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, Z, I, I,
                                     I, I, S3, S3, S3, S3, S3, S3, S3, S3, F, I, I, I, P]
     for f in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
-              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_fwd_fp8", "sdpa_fwd_fp8_varlen"):
+              "sdpa_bwd_ex", "sdpa_bwd_ex_noalloc", "sdpa_bwd_varlen", "sdpa_fwd_fp8",
+              "sdpa_fwd_fp8_varlen"):
         getattr(lib, f).restype = I
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.restype = ctypes.c_char_p
@@ -294,6 +297,42 @@ def bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = 
                          _strides(o, 4), _strides(dout, 4), _strides(dq, 4), _strides(dk, 4),
                          _strides(dv, 4), scale, int(bool(causal)), int(bool(bottom_right)),
                          int(window_left), _stream(stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, *, scale: Optional[float] = None,
+                causal: bool = False, bottom_right: bool = False, window_left: int = -1,
+                stream=None):
+    """Dense backward into the caller's dq, dk, dv, with the library's fixed
+    per-device workspace instead of one passed in (sdpa_bwd_ex_noalloc): no
+    device memory is allocated, here or in the library. Calls that overlap on
+    one device race on that workspace. Returns (dq, dk, dv)."""
+    lib = _load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("dense path expects 4-D (b, h, s, d) tensors")
+    b, h, s_q, d = q.shape
+    h_kv, s_kv = k.shape[1], k.shape[2]
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(k.shape) != (b, h_kv, s_kv, d) or tuple(v.shape) != (b, h_kv, s_kv, d):
+        raise ValueError("k/v shape mismatch")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, h, s_q):
+        raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
+    if dq is None or dk is None or dv is None:
+        raise ValueError("bwd_noalloc writes into caller-provided dq, dk and dv")
+    _on_one_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
+    _shape_like("dq", dq, q)
+    _shape_like("dk", dk, k)
+    _shape_like("dv", dv, v)
+    _same_dtype(q, k, v, o, dout, dq, dk, dv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.sdpa_bwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q), b, h, h_kv, s_q,
+                                 s_kv, d, _strides(q, 4), _strides(k, 4), _strides(v, 4),
+                                 _strides(o, 4), _strides(dout, 4), _strides(dq, 4),
+                                 _strides(dk, 4), _strides(dv, 4), scale, int(bool(causal)),
+                                 int(bool(bottom_right)), int(window_left), _stream(stream))
     _check(st)
     return dq, dk, dv
 

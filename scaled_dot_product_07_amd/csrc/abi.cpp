@@ -305,15 +305,25 @@ size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype) {
   return sdpa07::bwd_workspace_bytes((long long)b * h * s_q);
 }
 
-sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
-                        int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
-                        const int64_t k_stride[4], const int64_t v_stride[4],
-                        const int64_t o_stride[4], const int64_t do_stride[4],
-                        const int64_t dq_stride[4], const int64_t dk_stride[4],
-                        const int64_t dv_stride[4], float scale, int causal, int bottom_right,
-                        int window_left, void* stream) {
+static_assert(SDPA_BWD_FIXED_WORKSPACE_BYTES == sdpa07::kBwdFixedWorkspaceBytes &&
+                  SDPA_BWD_FIXED_WORKSPACE_ROWS == sdpa07::kBwdFixedWorkspaceRows,
+              "the header states the fixed workspace's size");
+
+namespace {
+
+// The dense backward of sdpa_bwd_ex and sdpa_bwd_ex_noalloc. With `fixed`,
+// `workspace` is ignored and the library's own per-device array takes its
+// place (looked up after every check has passed, so that a rejected call
+// touches no device state).
+sdpa_status bwd_dense(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, bool fixed, sdpa_dtype dtype,
+                      int b, int h, int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                      const int64_t k_stride[4], const int64_t v_stride[4],
+                      const int64_t o_stride[4], const int64_t do_stride[4],
+                      const int64_t dq_stride[4], const int64_t dk_stride[4],
+                      const int64_t dv_stride[4], float scale, int causal, int bottom_right,
+                      int window_left, void* stream, const char* what) {
   if (!valid_dtype(dtype)) return fail(SDPA_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dtype);
   if (dtype == SDPA_FP32)
     return fail(SDPA_ERR_UNSUPPORTED, "backward supports fp16 and bf16 io only");
@@ -342,14 +352,29 @@ sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void*
   if ((st = check_tile_span("v", v_stride[2], dtype)) != SDPA_OK) return st;
   if (qwork && kwork && !lse)
     return fail(SDPA_ERR_INVALID_ARG, "lse (the forward's statistic) is required");
-  if (qwork && kwork &&
-      (st = check_workspace(workspace, workspace_bytes, (long long)b * h * s_q)) != SDPA_OK)
+  const long long rows = (long long)b * h * s_q;
+  if (qwork && kwork && fixed && rows > sdpa07::kBwdFixedWorkspaceRows)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "%s: b * h * s_q = %lld query rows exceed the fixed workspace's %lld "
+                "(use sdpa_bwd_ex with a workspace of its own)",
+                what, rows, sdpa07::kBwdFixedWorkspaceRows);
+  if (qwork && kwork && !fixed &&
+      (st = check_workspace(workspace, workspace_bytes, rows)) != SDPA_OK)
     return st;
   const long long tq = (s_q + sdpa07::kBwdBlockM - 1) / sdpa07::kBwdBlockM;
   const long long tk = (s_kv + sdpa07::kBwdBlockN - 1) / sdpa07::kBwdBlockN;
   if ((long long)b * h * (tq > tk ? tq : tk) > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
   if (!work) return ok();
+  if (fixed) {
+    workspace = nullptr;
+    if (qwork && kwork) {
+      const hipError_t e = sdpa07::bwd_fixed_workspace(&workspace);
+      if (e != hipSuccess)
+        return fail(SDPA_ERR_LAUNCH, "%s: no fixed workspace on the current device: %s", what,
+                    hipGetErrorString(e));
+    }
+  }
 
   sdpa07::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
@@ -372,8 +397,39 @@ sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void*
             "window=%d\n",
             (int)dtype, b, h, h_kv, s_q, s_kv, d, causal, bottom_right, window_left);
   return launch_status(
-      sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, false, (hipStream_t)stream),
-      "sdpa_bwd");
+      sdpa07::launch_bwd(p, to_dt(dtype), d, causal != 0, false, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+sdpa_status sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, sdpa_dtype dtype, int b, int h,
+                        int h_kv, int s_q, int s_kv, int d, const int64_t q_stride[4],
+                        const int64_t k_stride[4], const int64_t v_stride[4],
+                        const int64_t o_stride[4], const int64_t do_stride[4],
+                        const int64_t dq_stride[4], const int64_t dk_stride[4],
+                        const int64_t dv_stride[4], float scale, int causal, int bottom_right,
+                        int window_left, void* stream) {
+  return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, false, dtype, b,
+                   h, h_kv, s_q, s_kv, d, q_stride, k_stride, v_stride, o_stride, do_stride,
+                   dq_stride, dk_stride, dv_stride, scale, causal, bottom_right, window_left,
+                   stream, "sdpa_bwd");
+}
+
+sdpa_status sdpa_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                sdpa_dtype dtype, int b, int h, int h_kv, int s_q, int s_kv,
+                                int d, const int64_t q_stride[4], const int64_t k_stride[4],
+                                const int64_t v_stride[4], const int64_t o_stride[4],
+                                const int64_t do_stride[4], const int64_t dq_stride[4],
+                                const int64_t dk_stride[4], const int64_t dv_stride[4],
+                                float scale, int causal, int bottom_right, int window_left,
+                                void* stream) {
+  return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, true, dtype, b, h, h_kv, s_q,
+                   s_kv, d, q_stride, k_stride, v_stride, o_stride, do_stride, dq_stride,
+                   dk_stride, dv_stride, scale, causal, bottom_right, window_left, stream,
+                   "sdpa_bwd_ex_noalloc");
 }
 
 sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -40,6 +40,8 @@
 // sequence's lengths from cu_seqlens; its statistic and workspace rows are
 // token-major (token * h + head).
 
+#include <mutex>
+
 #include "kernel_common.h"
 #include "sdpa_internal.h"
 
@@ -779,6 +781,32 @@ size_t bwd_workspace_bytes(long long rows) {
   // D (rows floats, padded to 64) then LSE in base 2 (rows floats)
   const size_t n = (size_t)((rows + 63) / 64 * 64);
   return ((2 * n * sizeof(float)) + 255) / 256 * 256;
+}
+
+// The fixed workspace: a file-scope device array, so that the code object
+// holds one copy per device from its load until the process ends. Host code
+// never passes the array's name to a kernel (on the host that name is only a
+// stand-in); it passes the device address looked up here.
+static __device__ __align__(256) unsigned char scratch[kBwdFixedWorkspaceBytes];
+
+hipError_t bwd_fixed_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, bool varlen,

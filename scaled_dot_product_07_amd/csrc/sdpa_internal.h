@@ -102,6 +102,18 @@ hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, bool varlen
 // row dot products rowsum(dO * O) and the statistic in base 2.
 size_t bwd_workspace_bytes(long long rows);
 
+// Backward workspace held in the library's own device code, for the entry
+// point that allocates nothing: 16 MiB on every device the library runs on,
+// enough for bwd_workspace_bytes(2^21 query rows).
+constexpr size_t kBwdFixedWorkspaceBytes = size_t(16) << 20;
+constexpr long long kBwdFixedWorkspaceRows = 1LL << 21;
+static_assert(kBwdFixedWorkspaceRows * 2 * sizeof(float) == kBwdFixedWorkspaceBytes,
+              "two fp32 values per query row");
+
+// Device address of the current device's copy of that workspace (looked up
+// once per device, then cached).
+hipError_t bwd_fixed_workspace(void** ptr);
+
 // Tile sizes of the dK/dV and dQ passes (for grid-size validation).
 constexpr int kBwdBlockM = 128;
 constexpr int kBwdBlockN = 128;

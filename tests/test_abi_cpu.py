@@ -31,8 +31,9 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("sdpa_fwd", "sdpa_fwd_ex", "sdpa_fwd_varlen", "sdpa_fwd_varlen_ex", "sdpa_bwd",
-              "sdpa_bwd_ex", "sdpa_bwd_varlen", "sdpa_fwd_fp8", "sdpa_fwd_fp8_varlen",
-              "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_version"):
+              "sdpa_bwd_ex", "sdpa_bwd_ex_noalloc", "sdpa_bwd_varlen", "sdpa_fwd_fp8",
+              "sdpa_fwd_fp8_varlen", "sdpa_bwd_workspace_size", "sdpa_last_error",
+              "sdpa_version"):
         assert s in syms
 
 
@@ -229,6 +230,43 @@ def test_bwd_ex_validation(lib, kw, status, msg):
                                 dict(window=0)])
 def test_bwd_ex_accepts_valid_options_without_work(lib, kw):
     assert bwd_ex(lib, b=0, **kw) == OK
+
+
+def bwd_noalloc(lib, h=2, h_kv=2, causal=1, br=0, window=-1, b=1, sq=8, skv=8, d=64,
+                dt=BF16):
+    qs = dense_st(b, h, sq, d)
+    ks = dense_st(b, h_kv, skv, d)
+    P = ALIGNED
+    return lib.sdpa_bwd_ex_noalloc(P, P, P, P, P, ALIGNED, P, P, P, dt, b, h, h_kv, sq, skv, d,
+                                   qs, ks, ks, qs, qs, qs, ks, ks, 0.1, causal, br, window, None)
+
+
+def test_bwd_noalloc_fixed_workspace_size_matches_the_header(lib):
+    text = open(HEADER).read()
+    assert "#define SDPA_BWD_FIXED_WORKSPACE_BYTES (16u << 20)" in text
+    assert "#define SDPA_BWD_FIXED_WORKSPACE_ROWS (1 << 21)" in text
+    # two fp32 values per query row: the largest accepted problem fills it exactly
+    assert lib.sdpa_bwd_workspace_size(1, 32, 1 << 16, 64, BF16) == 16 << 20
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    # one 64-row group past 2^21 query rows
+    (dict(h=32, sq=(1 << 16) + 2), UNSUPPORTED, "exceed the fixed workspace"),
+    (dict(b=3, h=16, sq=1 << 16), UNSUPPORTED, "exceed the fixed workspace"),
+    (dict(h=4, h_kv=3), INVALID, "multiple of h_kv"),
+    (dict(window=-5), INVALID, "window_left"),
+    (dict(dt=FP32), UNSUPPORTED, "fp16 and bf16"),
+    (dict(d=96), UNSUPPORTED, "head dim"),
+])
+def test_bwd_noalloc_validation(lib, kw, status, msg):
+    assert bwd_noalloc(lib, **kw) == status
+    assert msg in lib.sdpa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0, h_kv=0), dict(sq=0, skv=0)])
+def test_bwd_noalloc_without_work_is_ok(lib, kw):
+    """Nothing to compute: OK before any device lookup."""
+    assert bwd_noalloc(lib, **kw) == OK
 
 
 def bwd_varlen(lib, cu_q=ALIGNED, cu_kv=ALIGNED, n=2, tq=16, tkv=16, maxq=8, maxkv=8, h=2, h_kv=2,
