@@ -145,22 +145,28 @@ fwd16_kernel(FwdParams p) {
   // operand reads (ds_read_b128, 16 rows per phase) and the transposing P.V
   // operand reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes) hit
   // distinct banks; each lane loads the global chunk that its slot holds.
-  // Tile of step u lives in buffer u mod NBK (K) / u mod NBV (V); a step's
-  // loads run LK (K) and LV (V) steps ahead of the block that reads them.
+  // Tile u lives in buffer u mod NB of its ring (K or V). Step s reads K(s+1)
+  // and V(s-1) and loads K(s+NB) and V(s+NB-2) into the buffers its
+  // predecessor finished with, so every load has NB-1 steps to land before
+  // the wait that needs it. At d = 64 a ring of four (96 KB of LDS with the
+  // waves' Q rows) hides the latency of cold HBM reads; at d = 128 the LDS
+  // holds two.
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CH;         // rows per load instruction
   constexpr int CPT = BN / RPI / (NT / 64);  // load instructions per wave per tensor per step
   static_assert(CPT >= 1 && BN % (RPI * (NT / 64)) == 0, "tile/workgroup mismatch");
-  constexpr int NBK = 2, NBV = 2;
-  constexpr int LK = NBK - 1, LV = NBV - 1;
+  constexpr int NB = D <= 64 ? 4 : 2;
+  constexpr int LK = NB - 1, LV = NB - 1;  // steps between a tile's load and its read
+  // buffer of tile u >= -NB
+  auto ring = [](int u) -> int { return (int)((unsigned)(u + NB) % (unsigned)NB); };
   constexpr int TILE = BN * D;         // elements per tile
   constexpr int QROWS = 32 * D;        // elements of one wave's Q rows
-  constexpr int LDS_ELEMS = NBK * TILE + NBV * TILE + 8 * QROWS;
+  constexpr int LDS_ELEMS = 2 * NB * TILE + 8 * QROWS;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
-  T* const kbuf0 = lds;                          // [NBK][TILE]
-  T* const vbuf0 = lds + NBK * TILE;             // [NBV][TILE]
+  T* const kbuf0 = lds;                 // [NB][TILE]
+  T* const vbuf0 = lds + NB * TILE;     // [NB][TILE]
   // chunk permutation of row r (only r mod 16 matters)
   auto swz = [](int r) -> int {
     return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
@@ -318,7 +324,7 @@ fwd16_kernel(FwdParams p) {
   };
   const int full_k = tile_bytes(p.k_ss, BN), edge_k = tile_bytes(p.k_ss, edge_rows);
   const int full_v = tile_bytes(p.v_ss, BN), edge_v = tile_bytes(p.v_ss, edge_rows);
-  static_assert(LV == 1 && LK == 1, "step loads: V of the step's own tile, K two tiles ahead");
+  static_assert(LK == LV, "one load group per step: V(s-1+LV), then K(s+1+LK)");
   const int s_edge = n_full - 1 - LK;  // first step whose K tile is not a whole one
   auto tile_bytes_at = [&](int t, int full, int edge) -> int {
     return (t < 0 || t > n_full) ? 0 : t < n_full ? full : edge;
@@ -336,8 +342,7 @@ fwd16_kernel(FwdParams p) {
   };
   // this wave's load instruction x of tile u's K (V) into its buffer (u >= -1;
   // tile -1 is all zeros)
-  // (the buffer index: u mod NBK for K tile u, (u + NBV) mod NBV for V tile
-  // u >= -1; the fused blocks pass it in as a loop-invariant value)
+  // (the buffer index: ring(u) for tile u >= -1)
   auto kdma = [&](i32x4 r, int buf, int x) {
     dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T), kbuf0 + buf * TILE + RIT(x) * D);
   };
@@ -502,14 +507,18 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = M::mma(read_v(vb, t, db), p_last[t], acc[db]);
   };
-  static_assert(NBK == 2 && NBV == 2, "the blocks read buffer (s + 1) mod 2 of K and of V");
-  // rbuf = (s + 1) mod 2, passed in so that a loop over pairs of steps keeps
-  // the LDS operand addresses of both steps loop-invariant
+  // Buffers of step s: K(s+1) and V(s-1) are read, V(s-1+LV) and K(s+1+LK)
+  // written. With a ring of two all four are rbuf = (s + 1) mod 2 or its
+  // other one, passed in so that a loop over pairs of steps keeps the LDS
+  // operand addresses of both steps loop-invariant; a deeper ring adds a
+  // scalar buffer offset per step to the invariant lane addresses.
   auto block = [&](int s, int rbuf, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
                    const v8(&p_prev)[4],
                    v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) -> float {
-    const T* kb = kbuf0 + rbuf * TILE;  // K of step s+1
-    const T* vb = vbuf0 + rbuf * TILE;  // V of step s-1
+    const int kr = NB == 2 ? rbuf : ring(s + 1), vr = NB == 2 ? rbuf : ring(s - 1);
+    const int kw = NB == 2 ? rbuf ^ 1 : ring(s + 1 + LK), vw = NB == 2 ? rbuf ^ 1 : ring(s - 1 + LV);
+    const T* kb = kbuf0 + kr * TILE;  // K of step s+1
+    const T* vb = vbuf0 + vr * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
       if (i < NQK) return read_k(kb, i / 2, i % 2);
       return read_v(vb, (i - NQK) / (D / 32), (i - NQK) % (D / 32));
@@ -517,9 +526,8 @@ fwd16_kernel(FwdParams p) {
     auto mem = [&](int i) {  // loads of V(s-1+LV), then K(s+1+LK)
       const int k = i - MEM0;
       if (k < 0 || k >= 2 * CPT) return;
-      // V(s - 1 + LV) and K(s + 1 + LK) both go to buffer s mod 2 = rbuf ^ 1
-      if (k < CPT) vdma(rv, rbuf ^ 1, k);
-      else kdma(rk, rbuf ^ 1, k - CPT);
+      if (k < CPT) vdma(rv, vw, k);
+      else kdma(rk, kw, k - CPT);
     };
     const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
     float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
@@ -599,8 +607,8 @@ fwd16_kernel(FwdParams p) {
   // step reads, and one barrier (every wave's loads have then landed, and
   // every wave is done with the buffers this step's loads overwrite).
   auto step_begin = [&](int s, i32x4& rk, i32x4& rv) {
-    // both tiles whole unless the later one (K, tile s + 2) reaches the
-    // keys' edge tile (the V tile, s, is never before the first)
+    // both tiles whole unless the later one (K, tile s + 1 + LK) reaches the
+    // keys' edge tile (the V tile, s - 1 + LV >= 0, is never before the first)
     const int tk = s + 1 + LK, tv = s - 1 + LV;
     int bk = full_k, bv = full_v;
     if (__builtin_expect(s >= s_edge, 0)) {
@@ -632,9 +640,9 @@ fwd16_kernel(FwdParams p) {
     i32x4 rk, rv;
     step_begin(s, rk, rv);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) vdma(rv, (s - 1 + LV + NBV) % NBV, x);
+    for (int x = 0; x < CPT; ++x) vdma(rv, ring(s - 1 + LV), x);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) kdma(rk, (s + 1 + LK) % NBK, x);
+    for (int x = 0; x < CPT; ++x) kdma(rk, ring(s + 1 + LK), x);
   };
   // Step s with a block: the mask of this tile's scores where a band bound
   // cuts it, then the fused block; with checked offsets it returns the
@@ -714,7 +722,7 @@ fwd16_kernel(FwdParams p) {
   // K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2) (V(-1), read by a first block's
   // no-op P.V, is all zeros). Only Q and K(0) have to land before the first
   // block; the steps' own waits cover the rest.
-  T* const qbuf = lds + NBK * TILE + NBV * TILE + wave * QROWS;
+  T* const qbuf = lds + 2 * NB * TILE + wave * QROWS;
   {
     const int rows = wave_active ? min(q_len - row0, 32) : 0;
     const T* qb = Q + (int64_t)max(row0, 0) * p.q_ss;
@@ -736,11 +744,11 @@ fwd16_kernel(FwdParams p) {
     if (b - 1 + LV >= -1) {
       const i32x4 r = rsrc_v(b - 1 + LV);
 #pragma unroll
-      for (int x = 0; x < CPT; ++x) vdma(r, (b - 1 + LV + NBV) % NBV, x);
+      for (int x = 0; x < CPT; ++x) vdma(r, ring(b - 1 + LV), x);
     }
     const i32x4 r = rsrc_k(b + 1 + LK);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) kdma(r, (b + 1 + LK) % NBK, x);
+    for (int x = 0; x < CPT; ++x) kdma(r, ring(b + 1 + LK), x);
   }
   static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
   f32x16 sa[2], sb[2];
@@ -766,7 +774,7 @@ fwd16_kernel(FwdParams p) {
   // that tile (K(ws0) has landed at its barrier)
   for (; s < ws0; ++s) {
     light_step(s);
-    if (s == ws0 - 1) qk_only(kbuf0 + (ws0 % NBK) * TILE, sa);
+    if (s == ws0 - 1) qk_only(kbuf0 + ring(ws0) * TILE, sa);
   }
   // this wave's steps: even offsets from ws0 use S_cur = sa, S_next = sb,
   // P_prev = pb, P_cur = pa; odd ones the other way round
@@ -826,11 +834,12 @@ fwd16_kernel(FwdParams p) {
       }
     }
   }
-  // the P.V of the wave's last tile (its V is intact until two steps later),
-  // then its rows leave while the other waves go on
+  // the P.V of the wave's last tile (its V, in buffer (ws1 - 1) mod NB, is
+  // overwritten only by the loads of step ws1 + 1), then its rows leave while
+  // the other waves go on
   auto drain_and_store = [&]() {
     if (ws1 > ws0) {
-      const T* vb = vbuf0 + ((ws1 - 1) % NBV) * TILE;
+      const T* vb = vbuf0 + ring(ws1 - 1) * TILE;
       if (last_in_pa) pv_only(vb, pa);
       else pv_only(vb, pb);
     }
