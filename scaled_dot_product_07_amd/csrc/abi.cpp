@@ -261,7 +261,9 @@ sdpa_status sdpa_fwd_varlen_ex(const void* q, const void* k, const void* v, void
   if ((st = check_tile_span("k", k_stride[0], dtype)) != SDPA_OK) return st;
   if ((st = check_tile_span("v", v_stride[0], dtype)) != SDPA_OK) return st;
   const long long n_qtiles = (max_seqlen_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
-  if ((long long)num_seqs * h * n_qtiles > 0x7fffffffLL)
+  // one workgroup per live query tile (or pair of tiles) per head, bounded
+  // from the totals (the kernels find their units from cu_seqlens)
+  if (sdpa07::packed_units_per_head(total_q, num_seqs, sdpa07::kFwdBlockM) * h > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
   if (!work) return ok();
 
@@ -497,9 +499,10 @@ sdpa_status sdpa_bwd_varlen(const void* q, const void* k, const void* v, const v
   if (qwork && kwork &&
       (st = check_workspace(workspace, workspace_bytes, (long long)total_q * h)) != SDPA_OK)
     return st;
-  const long long tq = (max_seqlen_q + sdpa07::kBwdBlockM - 1) / sdpa07::kBwdBlockM;
-  const long long tk = (max_seqlen_kv + sdpa07::kBwdBlockN - 1) / sdpa07::kBwdBlockN;
-  if ((long long)num_seqs * h * (tq > tk ? tq : tk) > 0x7fffffffLL)
+  // one workgroup per live query tile (dQ) or key tile (dK, dV) per head,
+  // bounded from the totals (the kernels find their units from cu_seqlens)
+  if (sdpa07::packed_units_per_head(total_q, num_seqs, sdpa07::kBwdBlockM) * h > 0x7fffffffLL ||
+      sdpa07::packed_units_per_head(total_kv, num_seqs, sdpa07::kBwdBlockN) * h > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
   if (!work) return ok();
 
@@ -622,7 +625,9 @@ sdpa_status sdpa_fwd_fp8_varlen(const void* q, const void* k, const void* v, voi
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "lse: pointer is not 4-byte aligned");
   const long long n_qtiles = (max_seqlen_q + sdpa07::kFwdBlockM - 1) / sdpa07::kFwdBlockM;
-  if ((long long)num_seqs * h * n_qtiles > 0x7fffffffLL)
+  // one workgroup per live query tile (or pair of tiles) per head, bounded
+  // from the totals (the kernels find their units from cu_seqlens)
+  if (sdpa07::packed_units_per_head(total_q, num_seqs, sdpa07::kFwdBlockM) * h > 0x7fffffffLL)
     return fail(SDPA_ERR_INVALID_ARG, "grid exceeds int32");
   if (!work) return ok();
 

@@ -280,10 +280,30 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   // P of each pair and tile parity: [query block][register quad][lane][4]
   __shared__ __attribute__((aligned(16))) float pl[2][4][2 * 4 * 64 * 4];
 
-  const int nbh = p.b * p.h_kv;
-  const int kt = blockIdx.x / nbh;  // key tile; the first ones see the most queries
-  const int bh = blockIdx.x % nbh;
-  const int bi = bh / p.h_kv, hk = bh % p.h_kv;
+  // Dense: blockIdx -> (key tile, b*h_kv), the first key tiles (which a
+  // causal band shows to the most queries) first. Packed: blockIdx -> (live
+  // key tile of a sequence, K/V head), heads innermost, the tiles of all
+  // sequences in decreasing order of work (causal without a left bound: key
+  // tile t of a sequence costs n - t; other masks: the query count).
+  int kt, bi, hk;
+  if constexpr (VARLEN) {
+    hk = blockIdx.x % p.h_kv;
+    const bool taper = CAUSAL && p.window_left < 0;
+    const PackedUnit pu = packed_unit(blockIdx.x / p.h_kv, p.b, taper, [&](int s) -> int2 {
+      const int nk = (packed_len(p.cu_kv, s, p.total_kv) + kDkdvKeys - 1) / kDkdvKeys;
+      if (taper) return int2{nk, nk};
+      return int2{nk, max((packed_len(p.cu_q, s, p.total_q) + kDkdvQ - 1) / kDkdvQ, 1)};
+    });
+    if (pu.seq < 0) return;  // past the last key tile (uniform over the workgroup)
+    bi = pu.seq;
+    kt = pu.j;
+  } else {
+    const int nbh = p.b * p.h_kv;
+    kt = blockIdx.x / nbh;
+    const int bh = blockIdx.x % nbh;
+    bi = bh / p.h_kv;
+    hk = bh % p.h_kv;
+  }
   const int group = p.h / p.h_kv;  // query heads hk * group .. + group - 1 read this K/V head
   const Seq<VARLEN> sq(p, bi);
   if (kt * kDkdvKeys >= sq.kv_len) return;
@@ -526,11 +546,31 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
   __shared__ __attribute__((aligned(16))) T kl[2][BK * PITCH];
   __shared__ __attribute__((aligned(16))) T vl[2][BK * PITCH];
 
-  const int nbh = p.b * p.h;
-  const int n_qtiles = (p.s_q + kDqRows - 1) / kDqRows;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest causal tiles first
-  const int bh = blockIdx.x % nbh;
-  const int bi = bh / p.h, hi = bh % p.h;
+  // Dense: blockIdx -> (query tile, b*h), the heaviest causal tiles first.
+  // Packed: blockIdx -> (live query tile of a sequence, head), heads
+  // innermost, the tiles of all sequences in decreasing order of work
+  // (causal without a left bound: tile t costs t + 1; other masks: the keys).
+  int qt, bi, hi;
+  if constexpr (VARLEN) {
+    hi = blockIdx.x % p.h;
+    const bool taper = CAUSAL && p.window_left < 0;
+    const PackedUnit pu = packed_unit(blockIdx.x / p.h, p.b, taper, [&](int s) -> int2 {
+      const int nq = (packed_len(p.cu_q, s, p.total_q) + kDqRows - 1) / kDqRows;
+      if (taper) return int2{nq, nq};
+      return int2{nq, max((packed_len(p.cu_kv, s, p.total_kv) + kDqK - 1) / kDqK, 1)};
+    });
+    if (pu.seq < 0) return;  // past the last query tile (uniform over the workgroup)
+    bi = pu.seq;
+    const int nq = (packed_len(p.cu_q, bi, p.total_q) + kDqRows - 1) / kDqRows;
+    qt = taper ? nq - 1 - pu.j : pu.j;
+  } else {
+    const int nbh = p.b * p.h;
+    const int n_qtiles = (p.s_q + kDqRows - 1) / kDqRows;
+    qt = n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest causal tiles first
+    const int bh = blockIdx.x % nbh;
+    bi = bh / p.h;
+    hi = bh % p.h;
+  }
   const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
   const Seq<VARLEN> sq(p, bi);
   if (qt * kDqRows >= sq.q_len) return;
@@ -749,14 +789,17 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
   }
   // packed sequences with no queries (or no keys) still get their dK, dV
   // (or dQ) rows written as zeros by these two kernels
-  const long long gk = (long long)p.b * p.h_kv * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
+  const long long gk =
+      VARLEN ? packed_units_per_head(p.total_kv, p.b, kDkdvKeys) * p.h_kv
+             : (long long)p.b * p.h_kv * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
   if (gk > 0) {
     void* args[] = {&arg, &lse2};
     e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gk),
                         dim3(kDkdvThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  const long long gq = (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
+  const long long gq = VARLEN ? packed_units_per_head(p.total_q, p.b, kDqRows) * p.h
+                              : (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
   if (gq > 0) {
     void* args[] = {&arg, &lse2};
     e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gq),

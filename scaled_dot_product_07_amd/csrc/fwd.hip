@@ -173,10 +173,30 @@ fwd16_kernel(FwdParams p) {
   };
 
   // ---- work unit: two query tiles of one (b|sequence, h)
-  const int nbh = p.b * p.h;
-  int pair = (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
-  const int bi = bh / p.h, hi = bh % p.h;
+  // Dense: blockIdx -> (pair index, b*h). Packed: blockIdx -> (live pair of a
+  // sequence, head), heads innermost, pairs of all sequences heaviest first
+  // (the pair of a causal band without a left bound costs as many key blocks
+  // as its longer tile: n_qt - j for pair j; other masks: the keys).
+  const bool heavy_pair = CAUSAL && p.window_left < 0;
+  int pair, bi, hi;
+  if constexpr (VARLEN) {
+    hi = blockIdx.x % p.h;
+    const PackedUnit pu = packed_unit(blockIdx.x / p.h, p.b, heavy_pair, [&](int s) -> int2 {
+      const int lq = packed_len(p.cu_q, s, p.total_q);
+      const int np = (lq + 2 * BM - 1) / (2 * BM);
+      if (heavy_pair) return int2{np, (lq + BM - 1) / BM};
+      return int2{np, max((packed_len(p.cu_kv, s, p.total_kv) + BN - 1) / BN, 1)};
+    });
+    if (pu.seq < 0) return;  // past the last pair (uniform over the workgroup)
+    bi = pu.seq;
+    pair = pu.j;
+  } else {
+    const int nbh = p.b * p.h;
+    pair = (int)(blockIdx.x / nbh);
+    const int bh = blockIdx.x % nbh;
+    bi = bh / p.h;
+    hi = bh % p.h;
+  }
   const int hk = hi / (p.h / p.h_kv);  // K/V head of this query head
   int q_len, kv_len;
   int64_t q_off, k_off, v_off, o_off, lse_off, lse_st;
@@ -218,23 +238,12 @@ fwd16_kernel(FwdParams p) {
   const int hf = lane / 32, col = lane % 32;
 
   // the two tiles: causal without a left bound pairs (n-1-i, i), others
-  // (2i, 2i+1); a missing tile (odd count) is -1
-  const bool heavy_pair = CAUSAL && p.window_left < 0;
-  // Packed sequences pair the tiles of each sequence among themselves (its
-  // own tile count n_qt; units past its (n_qt + 1) / 2 pairs are empty), and
-  // take the pair indices from the top: only the longest sequences have the
-  // high ones, so their units, the longest, start first.
-  int n_qt = p.n_qtiles;
-  if constexpr (VARLEN) {
-    if (heavy_pair) {
-      n_qt = (q_len + BM - 1) / BM;
-      pair = (p.n_qtiles + 1) / 2 - 1 - pair;
-    }
-  }
-  int qt_a = heavy_pair ? n_qt - 1 - pair : 2 * pair;
-  if (VARLEN && heavy_pair && pair >= (n_qt + 1) / 2) qt_a = -1;
+  // (2i, 2i+1); a missing tile (odd count) is -1. Packed sequences pair the
+  // tiles of each sequence among themselves (its own tile count n_qt).
+  const int n_qt = VARLEN ? (q_len + BM - 1) / BM : p.n_qtiles;
+  const int qt_a = heavy_pair ? n_qt - 1 - pair : 2 * pair;
   const int qt_b0 = heavy_pair ? pair : 2 * pair + 1;
-  const int qt_b = (heavy_pair ? qt_b0 < qt_a : qt_b0 < p.n_qtiles) ? qt_b0 : -1;
+  const int qt_b = (heavy_pair ? qt_b0 < qt_a : qt_b0 < n_qt) ? qt_b0 : -1;
   // keys a tile's rows see: [lo, hi) (empty when the tile has no rows)
   auto tile_keys = [&](int qt, int& lo, int& hi2) {
     if (qt < 0 || qt * BM >= q_len) {
@@ -869,7 +878,7 @@ __global__ void __launch_bounds__(kFwdThreads) fwd32_kernel(FwdParams p) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float lds[2][2][BN * PITCH];
 
-  const Unit w = decode_unit<VARLEN>(p);
+  const Unit w = decode_unit<VARLEN, CAUSAL>(p);
   if (w.qt * BM >= w.q_len) return;
 
   const float* __restrict__ Q = (const float*)p.q + w.q_off;
@@ -1024,7 +1033,9 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   if (!fn) return hipErrorInvalidValue;
   // fp16/bf16: 8-wave workgroups over pairs of query tiles
   const bool paired = dt != Dt::F32;
-  const long long grid = (long long)(paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
+  const long long grid =
+      varlen ? packed_units_per_head(p.total_q, p.b, paired ? 2 * kFwdBlockM : kFwdBlockM) * p.h
+             : (long long)(paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};

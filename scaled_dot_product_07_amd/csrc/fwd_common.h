@@ -18,22 +18,37 @@ struct Unit {
   int64_t lse_off, lse_st;
 };
 
-template <bool VARLEN>
+// Dense: blockIdx -> (query tile, b*h) with the heaviest causal tiles first.
+// Packed: blockIdx -> (live tile of a sequence, head), heads innermost; the
+// tiles of all sequences come in decreasing order of work (a causal band
+// without a left bound: tile t of a sequence costs t + 1 key blocks; other
+// masks: its key count), a rank past the last tile gives q_len = 0.
+template <bool VARLEN, bool CAUSAL>
 __device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
   Unit w;
-  const int nbh = p.b * p.h;
-  const int u = blockIdx.x;
-  w.qt = p.n_qtiles - 1 - u / nbh;  // heaviest causal tiles first
-  const int bh = u % nbh;
-  const int bi = bh / p.h;
-  w.hi = bh % p.h;
   if constexpr (VARLEN) {
+    w.hi = blockIdx.x % p.h;
+    const bool taper = CAUSAL && p.window_left < 0;
+    const PackedUnit pu = packed_unit(blockIdx.x / p.h, p.b, taper, [&](int s) -> int2 {
+      const int nq = (packed_len(p.cu_q, s, p.total_q) + kFwdBlockM - 1) / kFwdBlockM;
+      if (taper) return int2{nq, nq};
+      const int nk = (packed_len(p.cu_kv, s, p.total_kv) + kFwdBlockN - 1) / kFwdBlockN;
+      return int2{nq, max(nk, 1)};
+    });
+    if (pu.seq < 0) {
+      w.qt = 0;
+      w.q_len = 0;  // no tile: the workgroup exits
+      return w;
+    }
+    const int bi = pu.seq;
     const int q0 = min(max(p.cu_q[bi], 0), p.total_q);
     const int q1 = min(max(p.cu_q[bi + 1], 0), p.total_q);
     const int k0 = min(max(p.cu_kv[bi], 0), p.total_kv);
     const int k1 = min(max(p.cu_kv[bi + 1], 0), p.total_kv);
     w.q_len = max(q1 - q0, 0);
     w.kv_len = max(k1 - k0, 0);
+    const int nq = (w.q_len + kFwdBlockM - 1) / kFwdBlockM;
+    w.qt = taper ? nq - 1 - pu.j : pu.j;
     w.q_off = (int64_t)q0 * p.q_ss + (int64_t)w.hi * p.q_sh;
     w.o_off = (int64_t)q0 * p.o_ss + (int64_t)w.hi * p.o_sh;
     w.k_off = (int64_t)k0 * p.k_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
@@ -41,6 +56,12 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
     w.lse_off = (int64_t)q0 * p.h + w.hi;
     w.lse_st = p.h;
   } else {
+    const int nbh = p.b * p.h;
+    const int u = blockIdx.x;
+    w.qt = p.n_qtiles - 1 - u / nbh;  // heaviest causal tiles first
+    const int bh = u % nbh;
+    const int bi = bh / p.h;
+    w.hi = bh % p.h;
     w.q_len = p.s_q;
     w.kv_len = p.s_kv;
     w.q_off = (int64_t)bi * p.q_sb + (int64_t)w.hi * p.q_sh;

@@ -109,7 +109,7 @@ fwd8_kernel(FwdParams p) {
   static_assert(CPT >= 1 && BN * CH % kF8Threads == 0, "tile does not split over the threads");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][BN * D];
 
-  const Unit w = decode_unit<VARLEN>(p);
+  const Unit w = decode_unit<VARLEN, CAUSAL>(p);
   if (w.qt * BM >= w.q_len) return;
   const unsigned char* __restrict__ Q = (const unsigned char*)p.q + w.q_off;
   const unsigned char* __restrict__ K = (const unsigned char*)p.k + w.k_off;
@@ -345,7 +345,8 @@ hipError_t launch_fwd_fp8(const FwdParams& p, Dt out, int d, bool causal, bool v
         hipLaunchKernel((const void*)&zero_float_kernel, dim3(1), dim3(1), za, 0, stream);
     if (e != hipSuccess) return e;
   }
-  const long long grid = (long long)p.n_qtiles * p.b * p.h;
+  const long long grid = varlen ? packed_units_per_head(p.total_q, p.b, kFwdBlockM) * p.h
+                                : (long long)p.n_qtiles * p.b * p.h;
   if (grid <= 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdint.h>
 
 namespace sdpa07 {
 namespace {
@@ -85,6 +86,120 @@ template <>
 __device__ __forceinline__ float dot2_ones<_Float16>(f16x2 h, float acc) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
   return __builtin_amdgcn_fdot2(h, one, acc, false);
+}
+
+// ---- live work units of a packed (THD) batch, heaviest first ---------------
+//
+// The grid of a packed launch is sized from totals the host knows (for
+// example total_q / 256 + num_seqs pairs of query tiles per head), never
+// from the lengths, which only the device holds. Each workgroup then finds
+// its own unit: sequence s holds n_s units, and unit j of it costs a_s - j
+// (taper: the causal tiles, whose key ranges shrink with j; a_s >= n_s) or
+// a_s (flat). Units are taken in decreasing order of cost (ties by sequence,
+// then j), so the longest start first and the last to start are short. The
+// rank u of a unit in that order is inverted by a binary search on the cost:
+// C(k) = number of units costing at least k, a sum over sequences taken 64
+// at a time with one wave reduction; then the sequence holding the
+// (u - C(k* + 1))-th unit of cost k* by a prefix sum. Ranks past the last
+// unit give seq = -1. Every lane of the calling wave takes part and receives
+// the same result.
+struct PackedUnit {
+  int seq;
+  int j;
+};
+
+// (the totals are returned through readfirstlane, so that the compiler
+// keeps them, and the control flow that depends on them, scalar)
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  const int lane = threadIdx.x % 64;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// units_of(s) returns int2{n_s, a_s} for sequence s < nseq.
+template <typename F>
+__device__ PackedUnit packed_unit(int u, int nseq, bool taper, F&& units_of) {
+  const int lane = threadIdx.x % 64;
+  auto cnt = [&](int n, int a, int k) -> int {
+    return taper ? min(max(a - k + 1, 0), n) : (a >= k ? n : 0);
+  };
+  // the first 64 sequences are read once; later ones on every pass
+  int n0 = 0, a0 = 0;
+  if (lane < nseq) {
+    const int2 na = units_of(lane);
+    n0 = na.x;
+    a0 = na.y;
+  }
+  auto count_ge = [&](int k) -> int {
+    int c = cnt(n0, a0, k);
+    for (int s0 = 64; s0 < nseq; s0 += 64) {
+      if (s0 + lane < nseq) {
+        const int2 na = units_of(s0 + lane);
+        c += cnt(na.x, na.y, k);
+      }
+    }
+    return wave_sum_i(c);
+  };
+  int amax = n0 > 0 ? a0 : 0;
+  for (int s0 = 64; s0 < nseq; s0 += 64) {
+    if (s0 + lane < nseq) {
+      const int2 na = units_of(s0 + lane);
+      if (na.x > 0) amax = max(amax, na.y);
+    }
+  }
+  amax = wave_max_i(amax);
+  if (amax <= 0 || u >= count_ge(1)) return {-1, 0};
+  int lo = 1, hi = amax;  // C(lo) > u >= C(hi + 1)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) > u) lo = mid;
+    else hi = mid - 1;
+  }
+  int r = u - count_ge(lo + 1);  // rank among the units of cost exactly lo
+  for (int s0 = 0; s0 < nseq; s0 += 64) {
+    int n = n0, a = a0;
+    if (s0 > 0) {
+      n = a = 0;
+      if (s0 + lane < nseq) {
+        const int2 na = units_of(s0 + lane);
+        n = na.x;
+        a = na.y;
+      }
+    }
+    const int e = cnt(n, a, lo) - cnt(n, a, lo + 1);
+    const int incl = wave_incl_scan_i(e);
+    const int tot = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    if (r < tot) {
+      const unsigned long long m = __ballot(incl > r);
+      const int first = __builtin_amdgcn_readfirstlane(__ffsll((long long)m) - 1);
+      const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - e, first));
+      const int af = __builtin_amdgcn_readfirstlane(__shfl(a, first));
+      return {s0 + first, taper ? af - lo : r - excl};
+    }
+    r -= tot;
+  }
+  return {-1, 0};
+}
+
+// Clamped length of packed sequence s: cu[s + 1] - cu[s] within [0, total].
+__device__ __forceinline__ int packed_len(const int32_t* cu, int s, int total) {
+  const int a = min(max(cu[s], 0), total);
+  const int b = min(max(cu[s + 1], 0), total);
+  return max(b - a, 0);
 }
 
 }  // namespace

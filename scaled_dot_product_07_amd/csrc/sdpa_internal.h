@@ -85,6 +85,14 @@ constexpr int kFwdBlockN = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;    // fp32 forward workgroup
 constexpr int kFwdThreads16 = 512;  // fp16/bf16 forward workgroup (two key groups)
 
+// Workgroups per head of a packed (THD) launch whose units hold unit_rows
+// query rows of one sequence (a 128-row tile, or a pair of them): every split
+// of total rows into num_seqs sequences has at most total / unit_rows +
+// num_seqs such units, so the grid needs no lengths from the device.
+constexpr long long packed_units_per_head(long long total, long long num_seqs, int unit_rows) {
+  return total / unit_rows + num_seqs;
+}
+
 // Enqueue the forward; returns the launch status.
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
                       hipStream_t stream);

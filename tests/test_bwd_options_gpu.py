@@ -155,6 +155,18 @@ VARLEN = [
     ([190, 64, 77], [190, 250, 30], 4, 4, 64, "bf16", False, True, 30),
     ([500, 131], [500, 131], 8, 2, 64, "fp16", True, False, 100),
 ]
+# Many sequences (more than one wave's 64 lanes, so the workgroups' unit
+# search reads cu_seqlens in chunks), some without queries or keys.
+_g = np.random.default_rng(91)
+_lq = _g.integers(0, 260, size=100)
+_lq[_g.random(100) < 0.15] = 0
+_lkv = _g.integers(0, 260, size=100)
+_lkv[_g.random(100) < 0.15] = 0
+VARLEN += [
+    (_lq.tolist(), _lq.tolist(), 2, 2, 64, "bf16", True, False, -1),
+    (_lq.tolist(), _lkv.tolist(), 4, 2, 64, "bf16", False, False, -1),
+    (_lq.tolist(), _lkv.tolist(), 2, 1, 128, "fp16", True, True, 50),
+]
 
 
 @pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"{c[5]}-h{c[2]}kv{c[3]}-d{c[4]}-"

@@ -61,10 +61,10 @@ def test_small_vs_oracle(gpu, case):
 @pytest.mark.parametrize("case", [("bf16", 64), ("fp16", 128)], ids=lambda c: "-".join(map(str, c)))
 def test_causal_pairs_within_each_sequence(gpu, case):
     """Causal units pair the query tiles of each sequence among themselves
-    (tile n_s-1-i with tile i of the sequence's own n_s tiles) and take the
-    longest sequences' pair indices first: every tile count from 0 to 9,
-    odd and even, in one pack, so that every pair slot is either a real
-    pair, a lone middle tile or empty for some sequence."""
+    (tile n_s-1-i with tile i of the sequence's own n_s tiles), and the
+    workgroups take the live pairs of all sequences heaviest first: every
+    tile count from 0 to 9, odd and even, in one pack, so that pairs, lone
+    middle tiles and sequences without tiles all occur."""
     dt, d = case
     lens = [1100, 0, 129, 700, 385, 1, 900, 256, 1024, 640, 513, 128, 64, 300, 830]
     announce(f"varlen causal tile pairs {case} lens={lens}")
@@ -82,6 +82,57 @@ def test_unequal_q_kv_lengths_and_dead_rows(gpu):
     for causal in (False, True):
         o, lse = _run(inp, 2, 64, 0.125, causal, gpu)
         _check_all(inp, o, lse, 0.125, causal, "bf16")
+
+
+LIVE_UNITS = [
+    # dtype, d, causal, window_left
+    ("bf16", 64, True, -1), ("bf16", 64, False, -1), ("fp16", 128, True, -1),
+    ("bf16", 64, True, 100), ("fp32", 64, True, -1), ("fp32", 128, False, -1),
+]
+
+
+@pytest.mark.parametrize("case", LIVE_UNITS, ids=lambda c: "-".join(map(str, c)))
+def test_many_sequences_live_units(gpu, case):
+    """150 sequences (more than one wave's 64 lanes, so the unit search reads
+    cu_seqlens in several chunks), a fifth of them empty, lengths 0 .. 400:
+    the grid holds total_q / 256 (or / 128) + num_seqs units per head and
+    each workgroup finds its unit on the device. Every row of every
+    sequence must be written (O and LSE start as sentinels) and match the
+    oracle; rows past the total stay untouched."""
+    import scaled_dot_product_07_amd as sdpa
+    dt, d, causal, window = case
+    g = np.random.default_rng(77 + d)
+    lens = g.integers(0, 401, size=150)
+    lens[g.random(150) < 0.2] = 0
+    lens = lens.tolist()
+    announce(f"varlen live units {case} n=150 T={sum(lens)}")
+    h = 2
+    inp = W.varlen_inputs(lens, lens, h, d, dt, seed=500 + d)
+    q, k, v = (x.to(gpu) for x in (inp.q, inp.k, inp.v))
+    o = torch.full_like(q, 77.0)
+    lse = torch.full((q.shape[0], h), 55.0, dtype=torch.float32, device=gpu)
+    sdpa.fwd_varlen(q, k, v, inp.cu_q.to(gpu), inp.cu_kv.to(gpu), max(lens), max(lens),
+                    total_q=inp.total_q, total_kv=inp.total_kv, scale=1 / np.sqrt(d),
+                    causal=causal, window_left=window, out=o, lse=lse)
+    torch.cuda.synchronize()
+    tq = inp.total_q
+    o_ref, lse_ref = oracle.fwd_varlen(f64(inp.q[:tq]), f64(inp.k[:tq]), f64(inp.v[:tq]),
+                                       inp.cu_q.numpy(), inp.cu_kv.numpy(), 1 / np.sqrt(d),
+                                       causal, window_left=window)
+    check_o(f64(o[:tq]), o_ref, dt)
+    check_lse(f64(lse[:tq]), lse_ref)
+    assert torch.all(o[tq:] == 77.0) and torch.all(lse[tq:] == 55.0)
+
+
+def test_one_live_sequence_among_many_empty(gpu):
+    """200 sequences of which only the 137th has rows: almost every workgroup
+    of the grid (total_q / 256 + 200 per head) finds no unit and exits."""
+    lens = [0] * 200
+    lens[137] = 700
+    announce("varlen one live sequence of 200")
+    inp = W.varlen_inputs(lens, lens, 3, 64, "bf16", seed=503)
+    o, lse = _run(inp, 3, 64, 0.125, True, gpu)
+    _check_all(inp, o, lse, 0.125, True, "bf16")
 
 
 def test_loose_max_seqlen_bound(gpu):
