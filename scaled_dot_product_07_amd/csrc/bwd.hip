@@ -50,6 +50,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPreThreads = 256;
+constexpr int kPreRows = 4;     // rows per lane group of the preprocess kernel
+// rows per block of the preprocess kernel: d / 8 lanes per row
+constexpr int pre_block_rows(int d) { return kPreThreads / (d / 8) * kPreRows; }
 constexpr int kBwdThreads = 256;
 constexpr int kDkdvThreads = 512;  // four wave pairs
 constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave pair)
@@ -98,43 +101,68 @@ struct Seq {
 };
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) in fp32 and LSE in base 2, row r of the statistic's
-// layout ((b, h, s_q) dense, (token, h) packed). D/8 lanes per row.
+// D = rowsum(dO * O) in fp32 and LSE in base 2 for every query row. A block
+// takes pre_block_rows(D) consecutive rows of one (b, h) (dense) or tokens of one
+// head (packed), so that its rows share their base offsets and a row's
+// address is one multiply; D/8 lanes per row, kPreRows rows per lane group,
+// all loads issued before the first product. Workspace row index: (b, h, s)
+// dense, token * h + head packed.
 template <typename T, int D, bool VARLEN>
-__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2,
-                                                               long long n) {
+__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int RPB = kPreThreads / LPR;
+  constexpr int kPreBlockRows = pre_block_rows(D);
+  static_assert(RPB * kPreRows == kPreBlockRows, "rows per block");
   const int tid = threadIdx.x;
-  const long long r = (long long)blockIdx.x * RPB + tid / LPR;
   const int sub = tid % LPR;
-  float acc = 0.f;
-  if (r < n) {
-    int64_t oo, go;
-    if constexpr (VARLEN) {
-      const long long tok = r / p.h;
-      const int hi = (int)(r % p.h);
-      oo = tok * p.o_ss + hi * p.o_sh;
-      go = tok * p.do_ss + hi * p.do_sh;
-    } else {
-      const int si = (int)(r % p.s_q);
-      const long long bh = r / p.s_q;
-      const int hi = (int)(bh % p.h), bi = (int)(bh / p.h);
-      oo = bi * p.o_sb + hi * p.o_sh + (long long)si * p.o_ss;
-      go = bi * p.do_sb + hi * p.do_sh + (long long)si * p.do_ss;
-    }
-    typedef T t8 __attribute__((ext_vector_type(8)));
-    const t8 ov = *(const t8*)((const T*)p.o + oo + sub * 8);
-    const t8 gv = *(const t8*)((const T*)p.dout + go + sub * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(to_f(ov[e]), to_f(gv[e]), acc);
+  // the block's (b, h) or head, and its first row within it
+  int rows, hi, row0;
+  int64_t ob, gb;
+  if constexpr (VARLEN) {
+    hi = blockIdx.x % p.h;
+    row0 = (int)(blockIdx.x / p.h) * kPreBlockRows;
+    rows = p.total_q;
+    ob = (int64_t)hi * p.o_sh;
+    gb = (int64_t)hi * p.do_sh;
+  } else {
+    const int nch = (p.s_q + kPreBlockRows - 1) / kPreBlockRows;
+    const int bh = blockIdx.x / nch;
+    row0 = (int)(blockIdx.x % nch) * kPreBlockRows;
+    hi = bh % p.h;
+    const int bi = bh / p.h;
+    rows = p.s_q;
+    ob = (int64_t)bi * p.o_sb + (int64_t)hi * p.o_sh;
+    gb = (int64_t)bi * p.do_sb + (int64_t)hi * p.do_sh;
   }
+  typedef T t8 __attribute__((ext_vector_type(8)));
+  t8 ov[kPreRows], gv[kPreRows];
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPR);
-  if (r < n && sub == 0) {
-    p.delta[r] = acc;
-    const float l = p.lse[r];
-    lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+  for (int k = 0; k < kPreRows; ++k) {
+    const int si = row0 + k * RPB + tid / LPR;
+    ov[k] = t8{};
+    gv[k] = t8{};
+    if (si < rows) {
+      ov[k] = *(const t8*)((const T*)p.o + ob + (int64_t)si * p.o_ss + sub * 8);
+      gv[k] = *(const t8*)((const T*)p.dout + gb + (int64_t)si * p.do_ss + sub * 8);
+    }
+  }
+  const long long st0 = VARLEN ? hi : (long long)(blockIdx.x / ((p.s_q + kPreBlockRows - 1) /
+                                                                 kPreBlockRows)) * p.s_q;
+  const int st = VARLEN ? p.h : 1;
+#pragma unroll
+  for (int k = 0; k < kPreRows; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(to_f(ov[k][e]), to_f(gv[k][e]), acc);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPR);
+    const int si = row0 + k * RPB + tid / LPR;
+    if (si < rows && sub == 0) {
+      const long long r = st0 + (long long)si * st;
+      p.delta[r] = acc;
+      const float l = p.lse[r];
+      lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
   }
 }
 
@@ -781,10 +809,12 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
   // the workspace: D for every query row (padded to 64), then LSE in base 2
   float* lse2 = p.delta + (n + 63) / 64 * 64;
   if (n > 0) {
-    const int rpb = kPreThreads / (D / 8);
-    void* args[] = {&arg, &lse2, (void*)&n};
-    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D, VARLEN>,
-                        dim3((unsigned)((n + rpb - 1) / rpb)), dim3(kPreThreads), args, 0, stream);
+    constexpr int BR = pre_block_rows(D);
+    const long long g = VARLEN ? (long long)p.h * ((p.total_q + BR - 1) / BR)
+                               : (long long)p.b * p.h * ((p.s_q + BR - 1) / BR);
+    void* args[] = {&arg, &lse2};
+    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D, VARLEN>, dim3((unsigned)g),
+                        dim3(kPreThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   // packed sequences with no queries (or no keys) still get their dK, dV
