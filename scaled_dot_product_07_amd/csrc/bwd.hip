@@ -201,18 +201,6 @@ __device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row
                             __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The same read from a tile of padded rows (PITCH elements, no permutation).
-template <typename T, int PITCH>
-__device__ __forceinline__ typename Mfma16<T>::v8 read_tr_padded(const T* base, int row, int colv) {
-  const T* a0 = base + row * PITCH + colv;
-  const i16x4 lo =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(a0 + 8 * PITCH));
-  return __builtin_bit_cast(typename Mfma16<T>::v8,
-                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // Packs 32 fp32 values held in a [2] x 16 MFMA C layout into 4 B operands
 // for a 64-deep contraction (element e of MFMA t: register 8(t%2)+e of block t/2).
 template <typename T>
@@ -381,8 +369,9 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   lg.init(tid, p.do_ss);
   i16x8 qr[LQ::CPT], gr[LQ::CPT];
   float l2r = 0.f, dlr = 0.f;
-  auto gload = [&](int it) {
-    const int hq = hk * group + it / nt, t = t_lo + it % nt;
+  // tile t of query head hq (the iterations step through the tiles of each
+  // head in turn; the loops keep (head, tile) counters, no divisions)
+  auto gload = [&](int hq, int t) {
     const int rows = sq.q_len - t * BQ;
     lq.load(qr, (const T*)p.q + sq.qoff(p.q_sb, p.q_sh, p.q_ss, hq) + (int64_t)t * BQ * p.q_ss,
             rows);
@@ -404,9 +393,15 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       dll[it & 1][tid] = dlr;
     }
   };
-  auto active = [&](int it) {  // the pair's keys see tile it (the same for both waves)
-    const int t = t_lo + it % nt;
+  auto active = [&](int t) {  // the pair's keys see query tile t (the same for both waves)
     return t >= wt_lo && t <= wt_hi;
+  };
+  // (head, tile) of the next iteration, from the current one
+  auto next = [&](int& h, int& t) {
+    if (++t == t_lo + nt) {
+      t = t_lo;
+      ++h;
+    }
   };
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
@@ -442,7 +437,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   };
 
   if (n_it > 0) {
-    gload(0);
+    gload(hk * group, t_lo);
     lstore(0, 0);
   }
   // Every load issued so far (the B-operand rows above all) has landed on
@@ -455,12 +450,14 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   // buffer it % 3 (kept as qs) and in the other buffers at parity it & 1.
   if (kside) {
     f32x16 x[2];
+    int tc = t_lo, hn = hk * group, tn = t_lo;  // tile of iteration it; head, tile of it + 1
+    next(hn, tn);
     for (int it = 0, qs = 0; it <= n_it; ++it) {
       const int qn = qs == 2 ? 0 : qs + 1;
-      if (it + 1 < n_it) gload(it + 1);
-      if (it < n_it && active(it)) {
+      if (it + 1 < n_it) gload(hn, tn);
+      if (it < n_it && active(tc)) {
         product(ql[qs], x);  // S = Q K^T
-        const int q_first = (t_lo + it % nt) * BQ;
+        const int q_first = tc * BQ;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -503,13 +500,18 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       if (it + 1 < n_it) lstore(it + 1, qn);
       __syncthreads();
       qs = qn;
+      tc = tn;
+      next(hn, tn);
     }
   } else {
     f32x16 x[2];  // dP - D of the previous tile
+    // tiles of iterations it - 1 and it; head, tile of it + 1
+    int tp = -1, tc = t_lo, hn = hk * group, tn = t_lo;
+    next(hn, tn);
     for (int it = 0, qs = 0, qp = 2; it <= n_it; ++it) {
       const int qn = qs == 2 ? 0 : qs + 1;
-      if (it + 1 < n_it) gload(it + 1);
-      if (it > 0 && active(it - 1)) {
+      if (it + 1 < n_it) gload(hn, tn);
+      if (it > 0 && active(tp)) {
         // dS = P (dP - D) of the previous tile, then dK^T += Q^T dS
         const float* pp = pl[(it - 1) & 1][pair];
 #pragma unroll
@@ -524,7 +526,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
           }
         accumulate(ql[qp], x);
       }
-      if (it < n_it && active(it)) {
+      if (it < n_it && active(tc)) {
         product(gl[it & 1], x);  // dP = dO V^T
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -540,6 +542,9 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       __syncthreads();
       qp = qs;
       qs = qn;
+      tp = tc;
+      tc = tn;
+      next(hn, tn);
     }
   }
 
@@ -565,14 +570,15 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdParams p, const float* lse2) {
-  // K and V tiles in padded rows: the permuted layout's per-chunk address
-  // registers do not fit this kernel's register budget at d = 128
-  constexpr int BK = kDqK, PITCH = D + 8;
+  // K and V tiles go from memory straight into double-buffered LDS (buffer
+  // loads with the LDS flag, no staging registers), in unpadded rows whose
+  // 16-byte chunks carry the chunk swizzle: the row reads (S^T, dP^T) and
+  // the transposing reads (K^T) are both free of bank conflicts.
+  constexpr int BK = kDqK;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  using LK = TileLoader<T, D, BK, kBwdThreads, false>;
-  __shared__ __attribute__((aligned(16))) T kl[2][BK * PITCH];
-  __shared__ __attribute__((aligned(16))) T vl[2][BK * PITCH];
+  __shared__ __attribute__((aligned(16))) T kl[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T vl[2][BK * D];
 
   // Dense: blockIdx -> (query tile, b*h), the heaviest causal tiles first.
   // Packed: blockIdx -> (live query tile of a sequence, head), heads
@@ -646,27 +652,54 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
   const int wave_kv_end =
       row0 >= sq.q_len ? 0 : (CAUSAL ? min(sq.kv_len, w_last + shift + 1) : sq.kv_len);
   const int wave_kv_begin = row0 + shift - window;
-  LK lk, lv;
-  lk.init(tid, p.k_ss);
-  lv.init(tid, p.v_ss);
-  i16x8 kr[LK::CPT], vr[LK::CPT];
-  auto gload = [&](int j) {
-    lk.load(kr, K + (int64_t)j * BK * p.k_ss, sq.kv_len - j * BK);
-    lv.load(vr, V + (int64_t)j * BK * p.v_ss, sq.kv_len - j * BK);
+  // Load instruction x of wave w fills rows RIT(x) .. RIT(x) + RPI - 1 of a
+  // tile (1 KB of LDS); lane l fills row RIT(x) + l / CH, slot l % CH, with
+  // the global chunk that the slot holds under the row's swizzle. Rows past
+  // the keys read as zeros (the descriptor's byte bound ends with the last
+  // key row).
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;          // rows per load instruction
+  constexpr int NW = kBwdThreads / 64;  // waves
+  constexpr int CPT = BK / (RPI * NW);  // load instructions per wave per tensor
+  static_assert(CPT >= 1 && BK % (RPI * NW) == 0, "tile/workgroup mismatch");
+  static_assert((NW * RPI) % 16 == 0, "load rows change the swizzle phase");
+  auto RIT = [&](int x) { return (NW * x + wave) * RPI; };
+  const int drow = lane / CH;
+  const int dch = (lane % CH) ^ tile_swz<D>((RIT(0) + drow) % 16);  // RIT(x) mod 16: same for all x
+  const int kvoff = drow * (int)p.k_ss * (int)sizeof(T) + dch * 16;
+  const int vvoff = drow * (int)p.v_ss * (int)sizeof(T) + dch * 16;
+  auto tile_rsrc = [&](const T* base, int64_t stride, int j) -> i32x4 {
+    const int rows = min(sq.kv_len - j * BK, BK);
+    const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)stride + D) * (int)sizeof(T);
+    const unsigned long long a = (unsigned long long)(base + (int64_t)j * BK * stride);
+    return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
+  };
+  auto lds_addr = [](const T* x) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const T*)x;
+  };
+  auto gload = [&](int j, int buf) {
+    const i32x4 rk = tile_rsrc(K, p.k_ss, j), rv = tile_rsrc(V, p.v_ss, j);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rk, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T), lds_addr(kl[buf] + RIT(x) * D));
+#pragma unroll
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rv, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T), lds_addr(vl[buf] + RIT(x) * D));
   };
   const int vrow = 4 * hf + (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+  // chunk permutations of the rows this lane reads: rows 32kb + col for
+  // S^T and dP^T, rows 16t + vrow (+ 8) for the transposing K^T reads
+  const int sk = tile_swz<D>(col % 16), sk0 = tile_swz<D>(vrow), sk1 = tile_swz<D>(vrow + 8);
 
-  if (j1 > j0) {
-    gload(j0);
-    lk.store(kl[0], kr);
-    lv.store(vl[0], vr);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // as in the dK/dV kernel: the Q, dO rows have landed
+  if (j1 > j0) gload(j0, 0);
+  // The Q, dO rows above and the first tile have landed in every wave
+  // before the loop (the compiler cannot see the tile loads' completion).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
     const int buf = (j - j0) & 1;
-    if (j + 1 < j1) gload(j + 1);
+    if (j + 1 < j1) gload(j + 1, buf ^ 1);  // every wave is done with buf ^ 1
     const int kbase = j * BK;
     if (kbase < wave_kv_end && kbase + BK > wave_kv_begin) {
       const T* kb_ = kl[buf];
@@ -686,8 +719,8 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
         f32x16 sv = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const v8 ak = *(const v8*)&kb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
-          const v8 av = *(const v8*)&vb_[(32 * kb + col) * PITCH + 16 * ks + 8 * hf];
+          const v8 ak = read_row<T, D>(kb_, 32 * kb + col, 2 * ks + hf, sk);
+          const v8 av = read_row<T, D>(vb_, 32 * kb + col, 2 * ks + hf, sk);
           sv = M::mma(ak, qf[ks], sv);
           dp = M::mma(av, gf[ks], dp);
         }
@@ -718,15 +751,14 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const v8 ak = read_tr_padded<T, PITCH>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol);
+            const v8 ak = read_tr<T, D>(kb_, 16 * (2 * kb + t) + vrow, 32 * db + vcol, sk0, sk1);
             dq[db] = M::mma(ak, sb[t], dq[db]);
           }
       }
     }
-    if (j + 1 < j1) {
-      lk.store(kl[buf ^ 1], kr);
-      lv.store(vl[buf ^ 1], vr);
-    }
+    // this wave's loads of tile j + 1 have landed; after the barrier every
+    // wave's have, and every wave is done with buffer buf
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

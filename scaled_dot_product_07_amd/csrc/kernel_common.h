@@ -38,6 +38,24 @@ struct Mfma16<_Float16> {
   }
 };
 
+// One 16-byte-per-lane buffer load into LDS: lane l's 16 bytes land at LDS
+// byte address lds_addr + 16 l. Written as inline assembly so that the
+// compiler does not treat later LDS reads as dependent on it (it would wait
+// for every such load before each transposing read); the kernels place the
+// vmcnt waits themselves. M0, which the instruction takes its LDS address
+// from, is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsigned lds_addr) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+
 // Value of x held by the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float other_half(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
