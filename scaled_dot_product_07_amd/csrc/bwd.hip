@@ -233,40 +233,6 @@ __device__ __forceinline__ void pack_b1(const f32x16& x, typename Mfma16<T>::v8 
   }
 }
 
-// Loads one tile of `ROWS` rows x D of a (rows, d) tensor whose row r is at
-// base + r * stride, rows at or past `rows` reading as zeros. In LDS the
-// tile's rows are either permuted (SWZ: D elements, chunk c of row r at
-// c ^ tile_swz(r)) or padded (D + 8 elements, chunks in order).
-template <typename T, int D, int ROWS, int NT, bool SWZ>
-struct TileLoader {
-  static constexpr int CH = D / 8;
-  static constexpr int CPT = ROWS * CH / NT;
-  int roff[CPT], lrow[CPT], lofs[CPT];
-  __device__ void init(int tid, int64_t stride) {
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + NT * x;
-      lrow[x] = ch / CH;
-      roff[x] = lrow[x] * (int)stride * (int)sizeof(T) + (ch % CH) * 16;
-      lofs[x] = SWZ ? lrow[x] * D + (((ch % CH) ^ tile_swz<D>(lrow[x])) << 3)
-                    : lrow[x] * (D + 8) + (ch % CH) * 8;
-    }
-  }
-  __device__ void load(i16x8 (&reg)[CPT], const T* tile_base, int rows) const {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tile_base, (short)0, 0x7fffffff, kBufferFlags);
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int off = lrow[x] < rows ? roff[x] : kOutOfRange;
-      reg[x] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    }
-  }
-  __device__ void store(T* lds, const i16x8 (&reg)[CPT]) const {
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) *(i16x8*)&lds[lofs[x]] = reg[x];
-  }
-};
-
 // ---------------------------------------------------------------------------
 // dK/dV: a pair of waves owns 32 keys of one K/V head, and the workgroup's
 // four pairs own 128 consecutive keys. The first wave of a pair (K side)
@@ -288,7 +254,6 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   constexpr int BQ = kDkdvQ;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
-  using LQ = TileLoader<T, D, BQ, kDkdvThreads, true>;
   __shared__ __attribute__((aligned(16))) T ql[3][BQ * D];
   __shared__ __attribute__((aligned(16))) T gl[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float l2l[2][BQ];
@@ -364,20 +329,50 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
 
   // iteration it covers query head hk * group + it / nt, tile t_lo + it % nt
   const int n_it = group * nt;
-  LQ lq, lg;
-  lq.init(tid, p.q_ss);
-  lg.init(tid, p.do_ss);
-  i16x8 qr[LQ::CPT], gr[LQ::CPT];
+  // Q and dO tiles go from memory straight into LDS (buffer loads with the
+  // LDS flag) in unpadded rows with the chunk swizzle: load instruction x of
+  // wave w fills rows RIT(x) .. RIT(x) + RPI - 1 (1 KB), lane l row
+  // RIT(x) + l / CH, slot l % CH, with the global chunk that the slot holds.
+  // Rows past the sequence read as zeros (the descriptor's byte bound).
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;            // rows per load instruction
+  constexpr int NW = kDkdvThreads / 64;   // waves
+  constexpr int CPT = BQ / (RPI * NW);    // load instructions per wave per tensor
+  static_assert(CPT >= 1 && BQ % (RPI * NW) == 0, "tile/workgroup mismatch");
+  static_assert((NW * RPI) % 16 == 0, "load rows change the swizzle phase");
+  auto RIT = [&](int x) { return (NW * x + wave) * RPI; };
+  const int drow = lane / CH;
+  const int dch = (lane % CH) ^ tile_swz<D>((RIT(0) + drow) % 16);  // RIT(x) mod 16: same for all x
+  const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + dch * 16;
+  const int gvoff = drow * (int)p.do_ss * (int)sizeof(T) + dch * 16;
+  auto tile_rsrc = [&](const T* tile, int64_t stride, int rows) -> i32x4 {
+    const int bytes = rows <= 0 ? 0 : ((min(rows, BQ) - 1) * (int)stride + D) * (int)sizeof(T);
+    const unsigned long long a = (unsigned long long)tile;
+    return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
+  };
+  auto lds_addr = [](const T* x) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const T*)x;
+  };
   float l2r = 0.f, dlr = 0.f;
-  // tile t of query head hq (the iterations step through the tiles of each
-  // head in turn; the loops keep (head, tile) counters, no divisions)
-  auto gload = [&](int hq, int t) {
+  // tile t of query head hq into Q buffer qslot and dO buffer gslot (the
+  // iterations step through the tiles of each head in turn; the loops keep
+  // (head, tile) counters, no divisions)
+  auto gload = [&](int hq, int t, int qslot, int gslot) {
     const int rows = sq.q_len - t * BQ;
-    lq.load(qr, (const T*)p.q + sq.qoff(p.q_sb, p.q_sh, p.q_ss, hq) + (int64_t)t * BQ * p.q_ss,
-            rows);
-    lg.load(gr,
-            (const T*)p.dout + sq.qoff(p.do_sb, p.do_sh, p.do_ss, hq) + (int64_t)t * BQ * p.do_ss,
-            rows);
+    const i32x4 rq =
+        tile_rsrc((const T*)p.q + sq.qoff(p.q_sb, p.q_sh, p.q_ss, hq) + (int64_t)t * BQ * p.q_ss,
+                  p.q_ss, rows);
+    const i32x4 rg = tile_rsrc(
+        (const T*)p.dout + sq.qoff(p.do_sb, p.do_sh, p.do_ss, hq) + (int64_t)t * BQ * p.do_ss,
+        p.do_ss, rows);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rq, qvoff, RIT(x) * (int)p.q_ss * (int)sizeof(T),
+                lds_addr(ql[qslot] + RIT(x) * D));
+#pragma unroll
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rg, gvoff, RIT(x) * (int)p.do_ss * (int)sizeof(T),
+                lds_addr(gl[gslot] + RIT(x) * D));
     if (tid < BQ) {
       const int qrow = t * BQ + tid;
       const int64_t si = sq.st0(p, hq) + (int64_t)qrow * st_step;
@@ -385,9 +380,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
       dlr = qrow < sq.q_len ? p.delta[si] : 0.f;
     }
   };
-  auto lstore = [&](int it, int qslot) {
-    lq.store(ql[qslot], qr);
-    lg.store(gl[it & 1], gr);
+  auto lstore = [&](int it) {  // the tile's statistic and D
     if (tid < BQ) {
       l2l[it & 1][tid] = l2r;
       dll[it & 1][tid] = dlr;
@@ -437,8 +430,8 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
   };
 
   if (n_it > 0) {
-    gload(hk * group, t_lo);
-    lstore(0, 0);
+    gload(hk * group, t_lo, 0, 0);
+    lstore(0);
   }
   // Every load issued so far (the B-operand rows above all) has landed on
   // every path into the loop; without this the compiler cannot tell, and
@@ -454,7 +447,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
     next(hn, tn);
     for (int it = 0, qs = 0; it <= n_it; ++it) {
       const int qn = qs == 2 ? 0 : qs + 1;
-      if (it + 1 < n_it) gload(hn, tn);
+      if (it + 1 < n_it) gload(hn, tn, qn, (it + 1) & 1);  // buffers free since the last barrier
       if (it < n_it && active(tc)) {
         product(ql[qs], x);  // S = Q K^T
         const int q_first = tc * BQ;
@@ -497,7 +490,9 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
                 float4{x[qb][4 * rq], x[qb][4 * rq + 1], x[qb][4 * rq + 2], x[qb][4 * rq + 3]};
         accumulate(gl[it & 1], x);  // dV^T += dO^T P
       }
-      if (it + 1 < n_it) lstore(it + 1, qn);
+      if (it + 1 < n_it) lstore(it + 1);
+      // this wave's tile loads have landed; after the barrier every wave's
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       qs = qn;
       tc = tn;
@@ -510,7 +505,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
     next(hn, tn);
     for (int it = 0, qs = 0, qp = 2; it <= n_it; ++it) {
       const int qn = qs == 2 ? 0 : qs + 1;
-      if (it + 1 < n_it) gload(hn, tn);
+      if (it + 1 < n_it) gload(hn, tn, qn, (it + 1) & 1);  // buffers free since the last barrier
       if (it > 0 && active(tp)) {
         // dS = P (dP - D) of the previous tile, then dK^T += Q^T dS
         const float* pp = pl[(it - 1) & 1][pair];
@@ -538,7 +533,9 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
             for (int e = 0; e < 4; ++e) x[qb][4 * rq + e] -= dd[e];
           }
       }
-      if (it + 1 < n_it) lstore(it + 1, qn);
+      if (it + 1 < n_it) lstore(it + 1);
+      // this wave's tile loads have landed; after the barrier every wave's
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       qp = qs;
       qs = qn;

@@ -15,10 +15,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.693147180559945309f;
-// Buffer resource word 3 for raw (untyped) loads on gfx9-family parts, and an
-// offset past any num_records bound (such loads return zeros).
+// Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kOutOfRange = (int)0x80000000u;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
