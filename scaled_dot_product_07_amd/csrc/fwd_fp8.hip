@@ -14,8 +14,8 @@
 //
 // One workgroup = 4 waves = one 128-row query tile of one (b, h) or
 // (sequence, h); each wave owns 32 query rows. Keys are streamed in tiles of
-// 64 rows of K and V through double-buffered, padded LDS (register-staged
-// loads of the next tile overlap the current one). Both products run on
+// 64 rows of K and V through double-buffered LDS, filled by direct-to-LDS
+// buffer loads of the next tile while the current one is computed. Both products run on
 // v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 accumulation), transposed as
 // in the fp16/bf16 kernel:
 //   S^T = K Q^T   A = 32 key rows x 64 d (two 16-byte LDS reads per lane),
@@ -105,8 +105,16 @@ fwd8_kernel(FwdParams p) {
       return 4 * (k & 1) + 2 * ((k >> 2) & 1) + ((k >> 1) & 1);
     }
   };
-  constexpr int CPT = BN * CH / kF8Threads;       // chunks per thread per tile
-  static_assert(CPT >= 1 && BN * CH % kF8Threads == 0, "tile does not split over the threads");
+  // K and V tiles go from memory straight into LDS (buffer loads with the
+  // LDS flag): a wave's load instruction fills 1 KB = RPI rows, lane l row
+  // RIT(x) + l / CH, slot l % CH, with the global chunk that the slot holds
+  // under the row's permutation; rows past the keys read as zeros (the
+  // descriptor's byte bound ends with the last key row)
+  constexpr int RPI = 1024 / D;                   // rows per load instruction
+  constexpr int NW = kF8Threads / 64;             // waves
+  constexpr int CPT = BN / (RPI * NW);            // load instructions per wave per tensor
+  static_assert(CPT >= 1 && BN % (RPI * NW) == 0, "tile does not split over the waves");
+  static_assert((NW * RPI) % 16 == 0, "load rows change the permutation phase");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][BN * D];
 
   const Unit w = decode_unit<VARLEN, CAUSAL>(p);
@@ -179,42 +187,38 @@ fwd8_kernel(FwdParams p) {
   const int v_chunk = (lane / 16) % 2, v_swz = swz(v_row);
   const int k_swz = swz(col);  // rows 32mb + col
 
-  i32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + kF8Threads * x;
-      const int r = ch / CH, cc = ch % CH;
-      const int key = j * BN + r;
-      if (key < w.kv_len) {
-        kreg[x] = *(const i32x4*)(K + (int64_t)key * p.k_ss + cc * 16);
-        vreg[x] = *(const i32x4*)(V + (int64_t)key * p.v_ss + cc * 16);
-      } else {
-        kreg[x] = i32x4{};
-        vreg[x] = i32x4{};
-      }
-    }
+  auto RIT = [&](int x) { return (NW * x + wave) * RPI; };
+  const int drow = lane / CH;
+  const int dch = (lane % CH) ^ swz((RIT(0) + drow) % 16);  // RIT(x) mod 16: same for all x
+  const int kvoff = drow * (int)p.k_ss + dch * 16;
+  const int vvoff = drow * (int)p.v_ss + dch * 16;
+  auto tile_rsrc = [&](const unsigned char* base, int64_t stride, int j) -> i32x4 {
+    const int rows = min(w.kv_len - j * BN, BN);
+    const int bytes = rows <= 0 ? 0 : (rows - 1) * (int)stride + D;
+    const unsigned long long a = (unsigned long long)(base + (int64_t)j * BN * stride);
+    return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferFlags};
   };
-  auto store_tile = [&](int buf) {
+  auto lds_addr = [](const unsigned char* x) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const unsigned char*)x;
+  };
+  auto load_tile = [&](int j, int buf) {
+    const i32x4 rk = tile_rsrc(K, p.k_ss, j), rv = tile_rsrc(V, p.v_ss, j);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int ch = tid + kF8Threads * x;
-      const int r = ch / CH, cc = ch % CH;
-      const int at = r * D + ((cc ^ swz(r)) << 4);
-      *(i32x4*)&lds[buf][0][at] = kreg[x];
-      *(i32x4*)&lds[buf][1][at] = vreg[x];
-    }
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rk, kvoff, RIT(x) * (int)p.k_ss, lds_addr(lds[buf][0] + RIT(x) * D));
+#pragma unroll
+    for (int x = 0; x < CPT; ++x)
+      lds_dma16(rv, vvoff, RIT(x) * (int)p.v_ss, lds_addr(lds[buf][1] + RIT(x) * D));
   };
 
-  if (j1 > j0) {
-    load_tile(j0);
-    store_tile(0);
-  }
+  if (j1 > j0) load_tile(j0, 0);
+  // the Q rows above and the first tile have landed in every wave
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = j0; j < j1; ++j) {
     const int buf = (j - j0) & 1;
-    if (j + 1 < j1) load_tile(j + 1);
+    if (j + 1 < j1) load_tile(j + 1, buf ^ 1);  // every wave is done with buf ^ 1
     const int kbase = j * BN;
     if (wave_active && kbase < wave_kv_end && kbase + BN > wave_kv_begin) {
       const unsigned char* kl = lds[buf][0];
@@ -283,7 +287,9 @@ fwd8_kernel(FwdParams p) {
       }
       lacc = mfma8(ones, pb, lacc);
     }
-    if (j + 1 < j1) store_tile(buf ^ 1);
+    // this wave's loads of tile j + 1 have landed; after the barrier every
+    // wave's have, and every wave is done with buffer buf
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
