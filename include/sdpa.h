@@ -18,8 +18,10 @@
  * innermost dimension is dense and whose base is 16-byte aligned.
  *
  * Conventions shared by every entry point
- *  - Every tensor pointer is a DEVICE pointer owned by the caller. The
- *    library allocates no device memory and keeps no pointer after return.
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. No call
+ *    allocates device memory, and none keeps a pointer after return (the
+ *    one fixed array the library holds is described at
+ *    sdpa_bwd_ex_noalloc).
  *  - Strides are in ELEMENTS. Dense tensors take 4 strides in logical
  *    (b, h, s, d) order, packed THD tensors 3 strides in (t, h, d) order. The
  *    d stride must be 1; every other stride, and every base pointer, must
@@ -31,7 +33,9 @@
  *  - Head dims d in {64, 128}.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues kernels on it and returns; nothing is synchronised and device
- *    memory is never read by the host. Calls are thread-safe.
+ *    memory is never read by the host. Calls are thread-safe, except that
+ *    overlapping sdpa_bwd_ex_noalloc calls on one device share its fixed
+ *    workspace.
  *  - A row with no visible key (s_kv = 0, or a packed sequence with no keys)
  *    gets O = 0 and LSE = -inf. Sizes of zero return SDPA_OK without
  *    launching.
@@ -85,13 +89,22 @@ sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* o, float
  *   cu_seqlens_q, cu_seqlens_kv: DEVICE int32 [num_seqs + 1], non-decreasing,
  *     cu[0] = 0, cu[num_seqs] <= total. Sequence n owns tokens
  *     [cu[n], cu[n+1]); positions (and the causal test) are local to it.
- *   max_seqlen_q: an upper bound on every query length (sizes the grid);
- *     max_seqlen_kv: an upper bound on every key length (checked only > 0).
+ *   max_seqlen_q, max_seqlen_kv: upper bounds on the query and key lengths
+ *     (checked > 0 and <= the totals; the kernels take the lengths
+ *     themselves from cu_seqlens).
  *   lse: fp32 (total_q, h) token-major contiguous; may be NULL.
+ * The grid holds total_q / 256 + num_seqs units per head (pairs of 128-row
+ * query tiles; total_q / 128 + num_seqs single tiles for fp32 and e4m3),
+ * a bound on the live units of any batch that meets the contract below;
+ * each workgroup finds its unit from cu_seqlens on the device, the units
+ * of all sequences in decreasing order of work.
  * The cu_seqlens contents are a caller contract (the host never reads them);
  * the kernels clamp every row index to [0, total) so rows at or beyond
  * total_q / total_kv (e.g. an allocation's capacity tail) are never read or
  * written, and query rows beyond a sequence's length are never written.
+ * Offsets that break the contract (decreasing, or summing past the totals)
+ * are still never followed outside [0, total), but rows of such a batch may
+ * be left unwritten.
  * Cited: cudnn-frontend PR #554 (THD packing with cu_seqlens and max_seqlen,
  * (T, H, 1) token-major statistic); its merge log, the FP8 d512 forward entry
  * (keys past the packed total must not feed P.V; dead rows get -inf).
@@ -284,8 +297,9 @@ sdpa_status sdpa_bwd_ex_noalloc(const void* q, const void* k, const void* v, con
  *     with its own (token, head) strides and d stride 1;
  *   lse: fp32 (total_q, h) token-major, as written by sdpa_fwd_varlen(_ex);
  *   cu_seqlens_q / cu_seqlens_kv, num_seqs, total_*, max_seqlen_*: as in
- *     sdpa_fwd_varlen (device int32 arrays of num_seqs + 1 entries;
- *     max_seqlen_* must be at least every sequence's length);
+ *     sdpa_fwd_varlen (device int32 arrays of num_seqs + 1 entries; the
+ *     dK/dV and dQ grids hold total / 128 + num_seqs tiles per head and
+ *     their workgroups find their tiles from cu_seqlens);
  *   workspace: sdpa_bwd_workspace_size(1, h, total_q, d, dtype) bytes.
  * Rows at or past total_q / total_kv are never read or written; rows of
  * sequences with no keys get dQ = 0, rows of sequences with no queries
