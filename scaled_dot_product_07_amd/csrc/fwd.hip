@@ -269,8 +269,8 @@ fwd16_kernel(FwdParams p) {
   // after the later of the two.
   constexpr int WAITN = CPT * (2 * LK - 2 < 2 * LV - 1 ? 2 * LK - 2 : 2 * LV - 1);
   using WaitStep = std::integral_constant<int, WAITN>;
-  // the prologue's loads issued after K(0): K(1 .. LK) and V(-1 .. LV-2)
-  using WaitK0 = std::integral_constant<int, CPT * (LK + LV)>;
+  // the prologue's loads issued after K(0) before its wait: V(-1) and K(1)
+  using WaitK0 = std::integral_constant<int, 2 * CPT>;
   using WaitAll = std::integral_constant<int, 0>;
 
   v8 qf[D / 16];
@@ -724,8 +724,9 @@ fwd16_kernel(FwdParams p) {
       dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T), qbuf + x * RPI * D);
     }
   }
-#pragma unroll
-  for (int b = -(LK + 1); b < 0; ++b) {
+  // the loads step b would have issued: V(b-1+LV) when it is a tile >= -1,
+  // then K(b+1+LK)
+  auto prologue_loads = [&](int b) {
     if (b - 1 + LV >= -1) {
       const i32x4 r = rsrc_v(b - 1 + LV);
 #pragma unroll
@@ -734,8 +735,15 @@ fwd16_kernel(FwdParams p) {
     const i32x4 r = rsrc_k(b + 1 + LK);
 #pragma unroll
     for (int x = 0; x < CPT; ++x) kdma(r, ring(b + 1 + LK), x);
-  }
-  static_assert(LV <= LK + 1, "prologue order assumes K(0) comes right after Q");
+  };
+  // Q, K(0) and the first block's V(-1), K(1) go first; the rest of the
+  // ring (needed from step 1 on) is issued after Q and K(0) have landed, so
+  // that with cold caches it does not compete with them for HBM. The issue
+  // order is that of the steps either way, which the counted waits rely on.
+  constexpr int B_LATE = -(LK + 1) + 2;  // first step whose loads wait
+  static_assert(LV == LK, "one load group per step");
+#pragma unroll
+  for (int b = -(LK + 1); b < (B_LATE < 0 ? B_LATE : 0); ++b) prologue_loads(b);
   f32x16 sa[2], sb[2];
   v8 pa[4], pb[4];
 #pragma unroll
@@ -745,6 +753,8 @@ fwd16_kernel(FwdParams p) {
   }
   wait_vm(WaitK0{});  // this wave's loads of Q and K(0); then every wave's
   __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int b = B_LATE; b < 0; ++b) prologue_loads(b);
   // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7]
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
