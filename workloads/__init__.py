@@ -93,6 +93,15 @@ def _draw(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
     return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
 
 
+def device_normal(shape, dtype: str, seed: int, device) -> torch.Tensor:
+    """iid N(0,1) drawn on the device by its own seeded generator (fp32, cast to
+    the io dtype): for inputs of several GiB, which the host would take long to
+    draw. Checks copy the parts they need back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(DTYPES[dtype])
+
+
 def dense_inputs(b: int, h: int, s_q: int, s_kv: int, d: int, dtype: str, layout: str,
                  seed: int, with_dout: bool = False) -> List[torch.Tensor]:
     """CPU tensors [q, k, v(, dout)] as logical (b, h, s, d) views of the physical layout."""
