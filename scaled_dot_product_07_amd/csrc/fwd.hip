@@ -323,7 +323,8 @@ fwd16_kernel(FwdParams p) {
   };
   auto dma = [&](i32x4 rs, int voff, int soff, T* dst) {
     lds_dma16(rs, voff, soff,
-              (unsigned)(size_t)(__attribute__((address_space(3))) T*)dst);
+              __builtin_amdgcn_readfirstlane(
+                  (unsigned)(size_t)(__attribute__((address_space(3))) T*)dst));
   };
   // this wave's load instruction x of tile u's K (V) into its buffer (u >= -1;
   // tile -1 is all zeros)
@@ -673,13 +674,64 @@ fwd16_kernel(FwdParams p) {
     }
   };
 
-  // Epilogue of a wave: combine the two lane halves' partial sums, normalise
-  // and store its rows (4 consecutive d per lane), and the statistic.
+  // Epilogue of a wave: combine the two lane halves' partial sums, normalise,
+  // and store its rows and the statistic. A lane holds 4-d pieces of its
+  // row's output spread over the row (the C layout of O^T); written straight
+  // out, every store instruction touches 32 rows with 16 bytes each. At
+  // d = 64 the rows go through the wave's own Q area instead (its Q is in
+  // registers by then): the lanes write their pieces into rows laid out
+  // [row][d], with the row's 16-byte chunks XOR-permuted by the row index so
+  // that the 32 rows of a write spread over the banks, then read back whole
+  // chunks, so that each store instruction writes 8 complete rows. (At
+  // d = 128 the kernel has no registers to spare for the exchange and keeps
+  // the direct stores.)
+  T* const qbuf = lds + 2 * NB * TILE + wave * QROWS;
   auto epilogue = [&]() {
     const float l_tot = l_run + other_half(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (q_valid) {
-      typedef T t4 __attribute__((ext_vector_type(4)));
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    if constexpr (D <= 64) {
+      constexpr int CPR = D / 8;     // 16-byte chunks per row
+      constexpr int RPS = 64 / CPR;  // rows per store instruction
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          t4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
+          *(t4*)&qbuf[col * D + ((4 * db + rq) ^ (col % CPR)) * 8 + 4 * hf] = ov;
+        }
+      // the wave reads back what its other lanes wrote: LDS operations of
+      // one wave complete in order; the fences keep the compiler's order and
+      // wait
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int sr = lane / CPR, sc = lane % CPR;
+      // the stores carry the system-scope cache policy (sc0 sc1), which
+      // writes the rows through to memory as they are stored; measured
+      // faster than leaving them dirty in the L2 for the kernel's end. They
+      // are buffer stores over the RPS rows of each instruction, whose
+      // per-lane offsets fit 31 bits unless a row stride is beyond 2^26
+      // elements (then plain stores).
+      const bool wt = p.o_ss < (1 << 26);
+#pragma unroll
+      for (int x = 0; x < 32 / RPS; ++x) {
+        const int r = x * RPS + sr;
+        const i32x4 v = *(const i32x4*)&qbuf[r * D + (sc ^ (r % CPR)) * 8];
+        if (wave_active && row0 + r < q_len) {
+          if (wt) {
+            const T* base = O + (int64_t)max(row0 + x * RPS, 0) * p.o_ss;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kBufferFlags),
+                (sr * (int)p.o_ss + sc * 8) * (int)sizeof(T), 0, kCacheSystemScope);
+          } else {
+            *(i32x4*)(O + (int64_t)(row0 + r) * p.o_ss + sc * 8) = v;
+          }
+        }
+      }
+    } else if (q_valid) {
       T* orow = O + (int64_t)qi * p.o_ss;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -690,10 +742,10 @@ fwd16_kernel(FwdParams p) {
           for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
           *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
         }
-      if (hf == 0 && p.lse)
-        p.lse[lse_off + (int64_t)qi * lse_st] =
-            l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
+    if (q_valid && hf == 0 && p.lse)
+      p.lse[lse_off + (int64_t)qi * lse_st] =
+          l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
   };
 
   if (n_steps == 0) {
@@ -707,7 +759,6 @@ fwd16_kernel(FwdParams p) {
   // K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2) (V(-1), read by a first block's
   // no-op P.V, is all zeros). Only Q and K(0) have to land before the first
   // block; the steps' own waits cover the rest.
-  T* const qbuf = lds + 2 * NB * TILE + wave * QROWS;
   {
     const int rows = wave_active ? min(q_len - row0, 32) : 0;
     const T* qb = Q + (int64_t)max(row0, 0) * p.q_ss;
@@ -756,10 +807,13 @@ fwd16_kernel(FwdParams p) {
 #pragma unroll
   for (int b = B_LATE; b < 0; ++b) prologue_loads(b);
   // Q rows as B operands of S^T = K Q^T: lane holds Q[qi][16ks + 8hf .. +7]
+  // (a negative scale is moved onto Q exactly: its sign bits flipped by a
+  // wave-uniform mask)
+  const int qsign = __builtin_amdgcn_readfirstlane(p.negate_q ? (int)0x80008000 : 0);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    i16x8 raw = *(const i16x8*)&qbuf[col * D + (((2 * ks + hf) ^ sk) * 8)];
-    if (p.negate_q) raw ^= (short)0x8000;  // a negative scale, moved onto Q exactly
+    i32x4 raw = *(const i32x4*)&qbuf[col * D + (((2 * ks + hf) ^ sk) * 8)];
+    raw ^= qsign;
     qf[ks] = __builtin_bit_cast(v8, raw);
   }
   if (ws1 > ws0 && ws0 == 0) qk_only(kbuf0, sa);  // S of step 0 (K(0) is in buffer 0)
@@ -840,9 +894,14 @@ fwd16_kernel(FwdParams p) {
     }
     epilogue();
   };
-  for (; s < n_steps; ++s) {
+  // the first step after the wave's own (step ws1, or step 0 for a wave
+  // without keys) brings its last V; it drains there, then only loads (kept
+  // out of the loop so that none of the store's addressing is hoisted into it)
+  if (s < n_steps) {
     light_step(s);
-    if (s == ws1 || (ws1 <= ws0 && s == 0)) drain_and_store();
+    ++s;
+    drain_and_store();
+    for (; s < n_steps; ++s) light_step(s);
   }
   // the steps' end: every wave's last loads have landed (and the final
   // barrier keeps the LDS alive for the waves still draining)

@@ -17,6 +17,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLn2 = 0.693147180559945309f;
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of a buffer store: sc0 | sc1 (system scope).
+constexpr int kCacheSystemScope = 1 | 16;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -41,8 +43,14 @@ struct Mfma16<_Float16> {
 // compiler does not treat later LDS reads as dependent on it (it would wait
 // for every such load before each transposing read); the kernels place the
 // vmcnt waits themselves. M0, which the instruction takes its LDS address
-// from, is saved and restored around it.
+// from, is saved and restored around it. The descriptor, the scalar offset
+// and the LDS address are wave-uniform by the callers' construction; they
+// pass through readfirstlane so that the scalar operands stay scalar
+// whatever the compiler's uniformity analysis concludes (a no-op on values
+// already in scalar registers).
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsigned lds_addr) {
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -50,7 +58,8 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsign
       "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 
