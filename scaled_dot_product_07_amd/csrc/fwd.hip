@@ -321,19 +321,19 @@ fwd16_kernel(FwdParams p) {
   auto tile_rsrc_at = [&](const T* __restrict__ tb, int t, int full, int edge) -> i32x4 {
     return make_rsrc(tb, tile_bytes_at(t, full, edge));
   };
-  auto dma = [&](i32x4 rs, int voff, int soff, T* dst) {
-    lds_dma16(rs, voff, soff,
-              __builtin_amdgcn_readfirstlane(
-                  (unsigned)(size_t)(__attribute__((address_space(3))) T*)dst));
-  };
+  // LDS byte address of the array's element e (the M0 operand of the
+  // direct-to-LDS loads), from the array's own LDS address
+  const unsigned lds_a = (unsigned)(size_t)(__attribute__((address_space(3))) T*)lds;
+  auto lds_at = [&](int e) -> unsigned { return lds_a + (unsigned)e * (unsigned)sizeof(T); };
+  auto dma = [&](i32x4 rs, int voff, int soff, unsigned dst) { lds_dma16(rs, voff, soff, dst); };
   // this wave's load instruction x of tile u's K (V) into its buffer (u >= -1;
   // tile -1 is all zeros)
   // (the buffer index: ring(u) for tile u >= -1)
   auto kdma = [&](i32x4 r, int buf, int x) {
-    dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T), kbuf0 + buf * TILE + RIT(x) * D);
+    dma(r, kvoff, RIT(x) * (int)p.k_ss * (int)sizeof(T), lds_at(buf * TILE + RIT(x) * D));
   };
   auto vdma = [&](i32x4 r, int buf, int x) {
-    dma(r, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T), vbuf0 + buf * TILE + RIT(x) * D);
+    dma(r, vvoff, RIT(x) * (int)p.v_ss * (int)sizeof(T), lds_at((NB + buf) * TILE + RIT(x) * D));
   };
   auto rsrc_k = [&](int u) -> i32x4 {
     return tile_rsrc_at(K0 + (int64_t)u * BN * p.k_ss, u, full_k, edge_k);
@@ -357,6 +357,15 @@ fwd16_kernel(FwdParams p) {
   //          produced
   constexpr bool CHECK_AFTER = D <= 64;
   float m_cur = -INFINITY, a_cur = 1.f, mx_nxt = -INFINITY;
+  // kept with m_cur: the offset a block subtracts (0 for a row without one)
+  // and the wave's rows without one (a scalar lane mask)
+  float m_off_cur = 0.f;
+  unsigned long long no_off = __builtin_amdgcn_ballot_w64(true);
+  auto set_m = [&](float m) {
+    m_cur = m;
+    m_off_cur = m == -INFINITY ? 0.f : m;
+    no_off = __builtin_amdgcn_ballot_w64(m == -INFINITY);
+  };
   constexpr int NPAIR = 16;  // 32 scores per lane, in pairs
   auto row_max = [&](const f32x16(&sv)[2]) -> float {
     float a = fmaxf(sv[0][0], sv[0][1]), b = fmaxf(sv[1][0], sv[1][1]);
@@ -383,7 +392,7 @@ fwd16_kernel(FwdParams p) {
   // had an offset, so r joins l. Otherwise fix raises the offset to the
   // tile's row max, rescales O and l and recomputes the tile's P.
   auto p_ok = [&](float r) -> bool {
-    return __builtin_amdgcn_ballot_w64(r > kSumMax || m_cur == -INFINITY) == 0;
+    return (__builtin_amdgcn_ballot_w64(r > kSumMax) | no_off) == 0;
   };
   auto fix = [&](const f32x16(&sv)[2], v8(&pv)[4]) {
     const float m_new = fmaxf(m_cur, row_max(sv) * c);
@@ -415,7 +424,7 @@ fwd16_kernel(FwdParams p) {
         asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
         acc[db][e] = x;
       }
-    m_cur = m_new;
+    set_m(m_new);
   };
   auto settle = [&](const f32x16(&sv)[2], v8(&pv)[4], float r) {
     if (__builtin_expect(p_ok(r), 1)) l_run += r;
@@ -431,7 +440,7 @@ fwd16_kernel(FwdParams p) {
     if (!__any(need)) return false;
     const float m_new = need ? mt : m_cur;
     a_cur = need ? fast_exp2(m_cur - m_new) : 1.f;  // 0 for a row's first offset
-    m_cur = m_new;
+    set_m(m_new);
     return true;
   };
 
@@ -515,7 +524,7 @@ fwd16_kernel(FwdParams p) {
       if (k < CPT) vdma(rv, vw, k);
       else kdma(rk, kw, k - CPT);
     };
-    const float m_off = m_cur == -INFINITY ? 0.f : m_cur;
+    const float m_off = m_off_cur;
     float r0 = 0.f, r1 = 0.f, mxa = -INFINITY, mxb = -INFINITY;
     i32x4 pk[4];
     auto slice = [&](int i) {
@@ -654,7 +663,7 @@ fwd16_kernel(FwdParams p) {
       if (any_cut)
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
-      if constexpr (FIRST) m_cur = row_max(s_cur) * c;  // the first tile's own row max
+      if constexpr (FIRST) set_m(row_max(s_cur) * c);  // the first tile's own row max
       return block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
     } else {
       float mx = mx_nxt;
@@ -772,7 +781,8 @@ fwd16_kernel(FwdParams p) {
     for (int x = 0; x < 32 / RPI; ++x) {
       const int qdchunk = (lane % CH) ^ swz((x * RPI + drow) % 16);
       const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + qdchunk * 16;
-      dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T), qbuf + x * RPI * D);
+      dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T),
+          lds_at(2 * NB * TILE + wave * QROWS + x * RPI * D));
     }
   }
   // the loads step b would have issued: V(b-1+LV) when it is a tile >= -1,
