@@ -200,6 +200,12 @@ sdpa_status sdpa_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
   p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_ss = o_stride[2];
   p.b = b; p.h = h; p.h_kv = h_kv; p.s_q = s_q; p.s_kv = s_kv;
   p.bottom_right = bottom_right; p.window_left = window_left;
+  // Options that describe the same band take the same schedule: a left
+  // window at least as wide as the longer side cuts no key (every row's
+  // lower bound i + shift - window is below key 0), and with equal sides, or
+  // with neither bound left, the alignment changes nothing.
+  if (p.window_left >= (s_q > s_kv ? s_q : s_kv)) p.window_left = -1;
+  if (p.window_left < 0 && (!causal || s_q == s_kv)) p.bottom_right = 0;
   p.n_qtiles = (int)n_qtiles;
   p.scale_log2 = scale_log2(scale);
   p.negate_q = scale < 0.f;

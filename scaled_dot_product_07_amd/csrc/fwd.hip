@@ -695,13 +695,33 @@ fwd16_kernel(FwdParams p) {
   // d = 128 the kernel has no registers to spare for the exchange and keeps
   // the direct stores.)
   T* const qbuf = lds + 2 * NB * TILE + wave * QROWS;
-  auto epilogue = [&]() {
+  // The epilogue in two parts at d = 64: epi_stage normalises the rows into
+  // the Q area and keeps the lane's statistic; epi_store reads the rows back
+  // and stores them with the statistic. Rows finished in the middle of the
+  // key loop are stored only after its last step: a global store counts in
+  // vmcnt like the loads, so a store in flight would hold up the wave's next
+  // counted wait (and through the barrier the workgroup) until memory has
+  // acknowledged it. (At d = 128 the rows are stored at once.)
+  int st_row0 = 0;          // the staged rows: first row, any row, and the
+  bool st_active = false;   // lane's row and statistic
+  bool st_qvalid = false;
+  float st_lse = 0.f;
+  auto epi_stage = [&]() {
     const float l_tot = l_run + other_half(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     typedef T t4 __attribute__((ext_vector_type(4)));
+    st_row0 = row0;
+    st_active = wave_active;
+    st_qvalid = q_valid;
+    st_lse = l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
     if constexpr (D <= 64) {
-      constexpr int CPR = D / 8;     // 16-byte chunks per row
-      constexpr int RPS = 64 / CPR;  // rows per store instruction
+      constexpr int CPR = D / 8;  // 16-byte chunks per row
+      // (the lane's offsets from a fresh copy of its index, so that each
+      // inlined copy computes them where it runs instead of sharing ones
+      // computed early and held in registers)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int cl = ln % 32, hl = ln / 32;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -709,15 +729,43 @@ fwd16_kernel(FwdParams p) {
           t4 ov;
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
-          *(t4*)&qbuf[col * D + ((4 * db + rq) ^ (col % CPR)) * 8 + 4 * hf] = ov;
+          *(t4*)&qbuf[cl * D + ((4 * db + rq) ^ (cl % CPR)) * 8 + 4 * hl] = ov;
         }
+    } else {
+      // (the output and statistic bases pass an empty asm for the same
+      // reason)
+      T* Ob = fresh_uniform(O);
+      float* lse_b = fresh_uniform(p.lse + lse_off);
+      if (q_valid) {
+        T* orow = Ob + (int64_t)qi * p.o_ss;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            t4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
+            *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
+          }
+        if (hf == 0 && p.lse) lse_b[(int64_t)qi * lse_st] = st_lse;
+      }
+    }
+  };
+  auto epi_store = [&]() {
+    if constexpr (D <= 64) {
+      constexpr int CPR = D / 8;     // 16-byte chunks per row
+      constexpr int RPS = 64 / CPR;  // rows per store instruction
+      T* Ob = fresh_uniform(O);
+      float* lse_b = fresh_uniform(p.lse + lse_off);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
       // the wave reads back what its other lanes wrote: LDS operations of
       // one wave complete in order; the fences keep the compiler's order and
       // wait
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int sr = lane / CPR, sc = lane % CPR;
+      const int sr = ln / CPR, sc = ln % CPR;
       // the stores carry the system-scope cache policy (sc0 sc1), which
       // writes the rows through to memory as they are stored; measured
       // faster than leaving them dirty in the L2 for the kernel's end. They
@@ -729,32 +777,23 @@ fwd16_kernel(FwdParams p) {
       for (int x = 0; x < 32 / RPS; ++x) {
         const int r = x * RPS + sr;
         const i32x4 v = *(const i32x4*)&qbuf[r * D + (sc ^ (r % CPR)) * 8];
-        if (wave_active && row0 + r < q_len) {
+        if (st_active && st_row0 + r < q_len) {
           if (wt) {
-            const T* base = O + (int64_t)max(row0 + x * RPS, 0) * p.o_ss;
+            const T* base = Ob + (int64_t)max(st_row0 + x * RPS, 0) * p.o_ss;
             __builtin_amdgcn_raw_buffer_store_b128(
                 v, __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kBufferFlags),
                 (sr * (int)p.o_ss + sc * 8) * (int)sizeof(T), 0, kCacheSystemScope);
           } else {
-            *(i32x4*)(O + (int64_t)(row0 + r) * p.o_ss + sc * 8) = v;
+            *(i32x4*)(Ob + (int64_t)(st_row0 + r) * p.o_ss + sc * 8) = v;
           }
         }
       }
-    } else if (q_valid) {
-      T* orow = O + (int64_t)qi * p.o_ss;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          t4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (T)(acc[db][4 * rq + e] * inv);
-          *(t4*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
-        }
+      if (st_qvalid && hf == 0 && p.lse) lse_b[(int64_t)(st_row0 + col) * lse_st] = st_lse;
     }
-    if (q_valid && hf == 0 && p.lse)
-      p.lse[lse_off + (int64_t)qi * lse_st] =
-          l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
+  };
+  auto epilogue = [&]() {
+    epi_stage();
+    epi_store();
   };
 
   if (n_steps == 0) {
@@ -896,13 +935,18 @@ fwd16_kernel(FwdParams p) {
   // the P.V of the wave's last tile (its V, in buffer (ws1 - 1) mod NB, is
   // overwritten only by the loads of step ws1 + 1), then its rows leave while
   // the other waves go on
-  auto drain_and_store = [&]() {
+  // (now: after the loop's last step, the rows are stored at once; before
+  // it they are staged and stored after it)
+  bool store_owed = false;
+  auto drain = [&](bool now) {
     if (ws1 > ws0) {
       const T* vb = vbuf0 + ring(ws1 - 1) * TILE;
       if (last_in_pa) pv_only(vb, pa);
       else pv_only(vb, pb);
     }
-    epilogue();
+    epi_stage();
+    if (now) epi_store();
+    else store_owed = true;
   };
   // the first step after the wave's own (step ws1, or step 0 for a wave
   // without keys) brings its last V; it drains there, then only loads (kept
@@ -910,14 +954,15 @@ fwd16_kernel(FwdParams p) {
   if (s < n_steps) {
     light_step(s);
     ++s;
-    drain_and_store();
+    drain(false);
     for (; s < n_steps; ++s) light_step(s);
   }
   // the steps' end: every wave's last loads have landed (and the final
   // barrier keeps the LDS alive for the waves still draining)
   wait_vm(WaitAll{});
   __builtin_amdgcn_s_barrier();
-  if (ws1 == n_steps && ws1 > ws0) drain_and_store();
+  if (ws1 == n_steps && ws1 > ws0) drain(true);
+  if (store_owed) epi_store();
 }
 
 // ---------------------------------------------------------------------------

@@ -63,6 +63,18 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, int soff, unsign
       : "memory");
 }
 
+// A wave-uniform pointer as a fresh scalar value: read from the first lane
+// and passed through an empty asm, so that address arithmetic on it is
+// done where it is used and not shared with (or hoisted to) earlier code.
+template <typename P>
+__device__ __forceinline__ P* fresh_uniform(P* ptr) {
+  const unsigned long long a = (unsigned long long)ptr;
+  unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return (P*)(((unsigned long long)hi << 32) | lo);
+}
+
 // Value of x held by the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float other_half(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);

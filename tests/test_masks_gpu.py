@@ -106,11 +106,9 @@ def test_varlen_options_vs_oracle(gpu, h, h_kv, causal, br, window):
 
 def test_option_defaults_match_plain_forward(gpu):
     """Options that change nothing on the headline-shaped workload: bottom-right
-    alignment with s_q == s_kv takes the same path (bit-identical); a window
-    wider than the keys is the same attention computed with another work
-    split (a left-bounded band pairs adjacent query tiles instead of splitting
-    the heavy tile of a causal pair), so it agrees to the rounding of the
-    output and of the fp32 partial sums."""
+    alignment with s_q == s_kv, and a window wider than the keys, describe
+    the same band, which the dense forward runs on the same schedule
+    (bit-identical results)."""
     import scaled_dot_product_07_amd as sdpa
     announce("fwd options defaults")
     c = W.FWD_BF16_B4H16S1024D64
@@ -120,6 +118,4 @@ def test_option_defaults_match_plain_forward(gpu):
     b3 = sdpa.fwd(q, k, v, scale=c.scale, causal=True, window_left=4096)   # wider than the keys
     torch.cuda.synchronize()
     assert torch.equal(a[0], b2[0]) and torch.equal(a[1], b2[1])
-    d_o = (a[0].float() - b3[0].float()).abs()
-    assert float(d_o.max()) <= 2.0 ** -7 * float(a[0].float().abs().max())
-    assert float((a[1] - b3[1]).abs().max()) <= 1e-3
+    assert torch.equal(a[0], b3[0]) and torch.equal(a[1], b3[1])
