@@ -107,6 +107,9 @@ namespace {
 // into Q would round c*Q to the io type and shift scores by up to 2^-9 of
 // their size.
 constexpr float kSumMax = 4096.f;
+// a compile-time ring phase (see the key loop's runs of four steps)
+template <int N>
+using kPh = std::integral_constant<int, N>;
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
@@ -507,11 +510,17 @@ fwd16_kernel(FwdParams p) {
   // other one, passed in so that a loop over pairs of steps keeps the LDS
   // operand addresses of both steps loop-invariant; a deeper ring adds a
   // scalar buffer offset per step to the invariant lane addresses.
-  auto block = [&](int s, int rbuf, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+  // (ph: the step's ring phase s mod 4 when known at compile time, which
+  // turns the ring buffers' offsets into constants; -1: computed from s)
+  auto block = [&](auto ph, int s, int rbuf, const f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
                    const v8(&p_prev)[4],
                    v8(&p_cur)[4], const i32x4& rk, const i32x4& rv) -> float {
-    const int kr = NB == 2 ? rbuf : ring(s + 1), vr = NB == 2 ? rbuf : ring(s - 1);
-    const int kw = NB == 2 ? rbuf ^ 1 : ring(s + 1 + LK), vw = NB == 2 ? rbuf ^ 1 : ring(s - 1 + LV);
+    constexpr int PH = decltype(ph)::value;
+    constexpr bool STATIC = PH >= 0 && NB == 4;
+    const int kr = NB == 2 ? rbuf : STATIC ? (PH + 1) & 3 : ring(s + 1);
+    const int vr = NB == 2 ? rbuf : STATIC ? (PH + 3) & 3 : ring(s - 1);
+    const int kw = NB == 2 ? rbuf ^ 1 : STATIC ? PH : ring(s + 1 + LK);
+    const int vw = NB == 2 ? rbuf ^ 1 : STATIC ? (PH + 2) & 3 : ring(s - 1 + LV);
     const T* kb = kbuf0 + kr * TILE;  // K of step s+1
     const T* vb = vbuf0 + vr * TILE;  // V of step s-1
     auto read_op = [&](int i) -> v8 {
@@ -649,7 +658,7 @@ fwd16_kernel(FwdParams p) {
   // (FIRST: the wave's first tile, a separate instantiation so that the row
   // max it takes, and the canonicalisation of the masked scores that it
   // needs, stay out of the other steps)
-  auto step = [&](auto first, int s, int rbuf, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
+  auto step = [&](auto first, auto ph, int s, int rbuf, f32x16(&s_cur)[2], f32x16(&s_nxt)[2],
                   const v8(&p_prev)[4], v8(&p_cur)[4]) -> float {
     constexpr bool FIRST = decltype(first)::value;
     i32x4 rk, rv;
@@ -664,7 +673,7 @@ fwd16_kernel(FwdParams p) {
         mask_tile<CAUSAL>(s_cur, kbase, qi, kv_len, hf, shift, window, cut_causal, cut_left,
                           cut_end);
       if constexpr (FIRST) set_m(row_max(s_cur) * c);  // the first tile's own row max
-      return block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
+      return block(ph, s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);  // P_cur still to settle
     } else {
       float mx = mx_nxt;
       if (any_cut) {
@@ -674,7 +683,7 @@ fwd16_kernel(FwdParams p) {
       }
       const bool rescale = decide(mx);
       const float a_blk = a_cur;
-      block(s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);
+      block(ph, s, rbuf, s_cur, s_nxt, p_prev, p_cur, rk, rv);
       if (rescale) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] *= a_blk;
@@ -878,6 +887,7 @@ fwd16_kernel(FwdParams p) {
   // P_prev = pb, P_cur = pa; odd ones the other way round
   using kFirst = std::true_type;
   using kNext = std::false_type;
+  using kDyn = std::integral_constant<int, -1>;
   bool last_in_pa = true;
   if (ws1 > ws0) {
     if constexpr (CHECK_AFTER) {
@@ -886,29 +896,68 @@ fwd16_kernel(FwdParams p) {
       // outside it (with the rest of its pair), so that the loop's code
       // holds no O rescale: one inside it made the register allocator move
       // O and P between two register sets, with a copy of both every step.
-      settle(sa, pa, step(kFirst{}, s, (s + 1) & 1, sa, sb, pb, pa));
+      settle(sa, pa, step(kFirst{}, kDyn{}, s, (s + 1) & 1, sa, sb, pb, pa));
       ++s;
+      // Pairs from odd offsets. With a ring of four and ws0 even, a pair
+      // that starts at a step s = 1 mod 4 begins a run of four steps whose
+      // ring phases 1, 2, 3, 0 are compile-time constants; other pairs
+      // (to reach that alignment, the last two or three steps, after an
+      // offset fix) compute their buffers from s.
+      const bool quads = NB == 4 && (ws0 & 1) == 0;
       while (s + 1 < ws1) {
         int ev = 0;  // 1: the pair's first tile needs fixing, 2: its second
         const int ba = (s + 1) & 1;  // the pairs' first steps read buffer ba
-        for (; s + 1 < ws1; s += 2) {
-          const float ra = step(kNext{}, s, ba, sb, sa, pa, pb);
+        if (quads && (s & 3) == 1) {
+          for (; s + 3 < ws1; s += 4) {
+            const float r1 = step(kNext{}, kPh<1>{}, s, ba, sb, sa, pa, pb);
+            if (__builtin_expect(!p_ok(r1), 0)) {
+              ev = 1;
+              break;
+            }
+            l_run += r1;
+            const float r2 = step(kNext{}, kPh<2>{}, s + 1, ba ^ 1, sa, sb, pb, pa);
+            if (__builtin_expect(!p_ok(r2), 0)) {
+              ev = 2;
+              break;
+            }
+            l_run += r2;
+            const float r3 = step(kNext{}, kPh<3>{}, s + 2, ba, sb, sa, pa, pb);
+            if (__builtin_expect(!p_ok(r3), 0)) {
+              ev = 3;
+              break;
+            }
+            l_run += r3;
+            const float r4 = step(kNext{}, kPh<0>{}, s + 3, ba ^ 1, sa, sb, pb, pa);
+            if (__builtin_expect(!p_ok(r4), 0)) {
+              ev = 4;
+              break;
+            }
+            l_run += r4;
+          }
+          if (ev > 2) {  // in the run's second pair
+            s += 2;
+            ev -= 2;
+          }
+        }
+        if (ev == 0) {
+          if (s + 1 >= ws1) break;
+          const float ra = step(kNext{}, kDyn{}, s, ba, sb, sa, pa, pb);
           if (__builtin_expect(!p_ok(ra), 0)) {
             ev = 1;
-            break;
+          } else {
+            l_run += ra;
+            const float rb = step(kNext{}, kDyn{}, s + 1, ba ^ 1, sa, sb, pb, pa);
+            if (__builtin_expect(!p_ok(rb), 0)) ev = 2;
+            else l_run += rb;
           }
-          l_run += ra;
-          const float rb = step(kNext{}, s + 1, ba ^ 1, sa, sb, pb, pa);
-          if (__builtin_expect(!p_ok(rb), 0)) {
-            ev = 2;
-            break;
+          if (ev == 0) {
+            s += 2;
+            continue;
           }
-          l_run += rb;
         }
-        if (ev == 0) break;
         if (ev == 1) {
           fix(sb, pb);  // tile s: scores in sb, P in pb
-          settle(sa, pa, step(kNext{}, s + 1, (s + 2) & 1, sa, sb, pb, pa));
+          settle(sa, pa, step(kNext{}, kDyn{}, s + 1, (s + 2) & 1, sa, sb, pb, pa));
         } else {
           fix(sa, pa);  // tile s + 1: scores in sa, P in pa
         }
@@ -916,18 +965,18 @@ fwd16_kernel(FwdParams p) {
       }
       last_in_pa = s >= ws1;
       if (s < ws1) {
-        settle(sb, pb, step(kNext{}, s, (s + 1) & 1, sb, sa, pa, pb));
+        settle(sb, pb, step(kNext{}, kDyn{}, s, (s + 1) & 1, sb, sa, pa, pb));
         ++s;
       }
     } else {
       const int ba = (s + 1) & 1;
       for (; s + 1 < ws1; s += 2) {
-        step(kNext{}, s, ba, sa, sb, pb, pa);
-        step(kNext{}, s + 1, ba ^ 1, sb, sa, pa, pb);
+        step(kNext{}, kDyn{}, s, ba, sa, sb, pb, pa);
+        step(kNext{}, kDyn{}, s + 1, ba ^ 1, sb, sa, pa, pb);
       }
       last_in_pa = s < ws1;
       if (s < ws1) {
-        step(kNext{}, s, (s + 1) & 1, sa, sb, pb, pa);
+        step(kNext{}, kDyn{}, s, (s + 1) & 1, sa, sb, pb, pa);
         ++s;
       }
     }
