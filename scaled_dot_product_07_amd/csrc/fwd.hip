@@ -6,16 +6,20 @@
 // top-left causal band; cudnn-frontend PR #554: statistic layouts and THD
 // packing with cu_seqlens).
 //
-// fp16/bf16: one workgroup = 8 waves over two 128-row query tiles of one
-// (b, h) or (sequence, h): waves 0-3 hold the rows of the first tile, 4-7
-// those of the second, 32 rows each, so every SIMD hosts one wave of each
-// (for a causal band without a left bound the tiles are paired heavy with
-// light, (n-1-i, i)). Each wave keeps, for its whole key range:
+// fp16/bf16: query tiles of 128 rows go in pairs of one (b, h) or
+// (sequence, h) (for a causal band without a left bound heavy with light,
+// (n-1-i, i)), 32 rows per wave. At d = 128 one workgroup of 8 waves runs
+// both tiles of a pair: waves 0-3 hold the rows of the first, 4-7 those of
+// the second, so every SIMD hosts one wave of each. At d = 64 each tile has
+// a workgroup of its own (4 waves, 80 KB of LDS, two per CU), and the grid
+// puts the two tiles of a pair where the dispatcher places two workgroups
+// on one CU, so that they still share its SIMDs but not a barrier. Each
+// wave keeps, for its whole key range:
 //   * its Q rows as MFMA B operands in VGPRs,
 //   * the fp32 output accumulator O^T (d x 32) in the MFMA C layout,
 //   * the offset m and running sum l of its rows.
-// Keys are streamed in tiles of 64 rows of K and V shared by all eight
-// waves, loaded by the buffer loads' direct-to-LDS path into double-buffered
+// Keys are streamed in tiles of 64 rows of K and V shared by all the
+// workgroup's waves, loaded by the buffer loads' direct-to-LDS path into double-buffered
 // LDS one step ahead of the block that reads them, with one barrier per
 // step. A wave computes over the steps its rows reach and only loads and
 // waits at the others; each wave sees every key tile of its rows, so no
@@ -54,6 +58,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fwd_common.h"
@@ -113,10 +118,12 @@ using kPh = std::integral_constant<int, N>;
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kFwdThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(fwd16_threads(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
-  constexpr int NT = kFwdThreads16;   // 8 waves
+  constexpr int NT = fwd16_threads(D);
+  constexpr int NW = NT / 64;          // waves: 4 (one query tile) or 8 (two)
+  constexpr bool SPLIT = NW == 4;
   // K and V tiles go from memory straight into LDS (buffer loads with the
   // LDS flag): a wave's load instruction fills 1 KB of LDS, lane l writing
   // bytes [16l, 16l + 16). Rows are stored unpadded and each row's 16-byte
@@ -127,7 +134,7 @@ fwd16_kernel(FwdParams p) {
   // Tile u lives in buffer u mod NB of its ring (K or V). Step s reads K(s+1)
   // and V(s-1) and loads K(s+NB) and V(s+NB-2) into the buffers its
   // predecessor finished with, so every load has NB-1 steps to land before
-  // the wait that needs it. At d = 64 a ring of four (96 KB of LDS with the
+  // the wait that needs it. At d = 64 a ring of four (80 KB of LDS with the
   // waves' Q rows) hides the latency of cold HBM reads; at d = 128 the LDS
   // holds two.
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -140,7 +147,7 @@ fwd16_kernel(FwdParams p) {
   auto ring = [](int u) -> int { return (int)((unsigned)(u + NB) % (unsigned)NB); };
   constexpr int TILE = BN * D;         // elements per tile
   constexpr int QROWS = 32 * D;        // elements of one wave's Q rows
-  constexpr int LDS_ELEMS = 2 * NB * TILE + 8 * QROWS;
+  constexpr int LDS_ELEMS = 2 * NB * TILE + NW * QROWS;
   using M = Mfma16<T>;
   using v8 = typename M::v8;
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
@@ -157,10 +164,26 @@ fwd16_kernel(FwdParams p) {
   // (the pair of a causal band without a left bound costs as many key blocks
   // as its longer tile: n_qt - j for pair j; other masks: the keys).
   const bool heavy_pair = CAUSAL && p.window_left < 0;
+  // One tile per workgroup: the grid runs in rounds of 2R workgroups (R =
+  // split_round, the compute-unit count); in a round, workgroup j < R takes
+  // the first tile of the round's pair unit j and workgroup R + j its second,
+  // the two that the dispatcher places on one CU when a full round is
+  // resident (measured on MI355X: workgroups i and i + 256 of a 512-workgroup
+  // grid at two per CU). The placement only matters for speed.
+  int unit = blockIdx.x, half = 0;
+  if constexpr (SPLIT) {
+    const int n_units = gridDim.x / 2;
+    const int R = p.split_round;
+    const int r = blockIdx.x / (2 * R);
+    const int rem = min(R, n_units - r * R);  // units in this round
+    const int off = blockIdx.x - r * 2 * R;
+    half = off / rem;
+    unit = r * R + off % rem;
+  }
   int pair, bi, hi;
   if constexpr (VARLEN) {
-    hi = blockIdx.x % p.h;
-    const PackedUnit pu = packed_unit(blockIdx.x / p.h, p.b, heavy_pair, [&](int s) -> int2 {
+    hi = unit % p.h;
+    const PackedUnit pu = packed_unit(unit / p.h, p.b, heavy_pair, [&](int s) -> int2 {
       const int lq = packed_len(p.cu_q, s, p.total_q);
       const int np = (lq + 2 * BM - 1) / (2 * BM);
       if (heavy_pair) return int2{np, (lq + BM - 1) / BM};
@@ -171,8 +194,8 @@ fwd16_kernel(FwdParams p) {
     pair = pu.j;
   } else {
     const int nbh = p.b * p.h;
-    pair = (int)(blockIdx.x / nbh);
-    const int bh = blockIdx.x % nbh;
+    pair = unit / nbh;
+    const int bh = unit % nbh;
     bi = bh / p.h;
     hi = bh % p.h;
   }
@@ -220,9 +243,14 @@ fwd16_kernel(FwdParams p) {
   // (2i, 2i+1); a missing tile (odd count) is -1. Packed sequences pair the
   // tiles of each sequence among themselves (its own tile count n_qt).
   const int n_qt = VARLEN ? (q_len + BM - 1) / BM : p.n_qtiles;
-  const int qt_a = heavy_pair ? n_qt - 1 - pair : 2 * pair;
-  const int qt_b0 = heavy_pair ? pair : 2 * pair + 1;
-  const int qt_b = (heavy_pair ? qt_b0 < qt_a : qt_b0 < n_qt) ? qt_b0 : -1;
+  const int qt_p = heavy_pair ? n_qt - 1 - pair : 2 * pair;
+  const int qt_q0 = heavy_pair ? pair : 2 * pair + 1;
+  const int qt_q = (heavy_pair ? qt_q0 < qt_p : qt_q0 < n_qt) ? qt_q0 : -1;
+  // the workgroup's tiles: A (waves 0-3) and B (waves 4-7), or with one tile
+  // per workgroup A only
+  const int qt_a = SPLIT && half ? qt_q : qt_p;
+  const int qt_b = SPLIT ? -1 : qt_q;
+  if (SPLIT && qt_a < 0) return;  // the pair has no second tile (uniform)
   // keys a tile's rows see: [lo, hi) (empty when the tile has no rows)
   auto tile_keys = [&](int qt, int& lo, int& hi2) {
     if (qt < 0 || qt * BM >= q_len) {
@@ -243,7 +271,7 @@ fwd16_kernel(FwdParams p) {
   const int t0 = kv_begin / BN;
   const int n_steps = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
 
-  const int qt = wave < 4 ? qt_a : qt_b;   // this wave's tile
+  const int qt = SPLIT || wave < 4 ? qt_a : qt_b;  // this wave's tile
   const int rg = wave % 4;                  // its row group
   const int row0 = qt * BM + rg * 32;       // first query row of this wave
   const int qi = row0 + col;                // this lane's query row
@@ -292,10 +320,10 @@ fwd16_kernel(FwdParams p) {
   // memory touched past the keys; a tile outside the keys is all zeros.
   // Load instruction x of wave w covers rows RIT(x) .. RIT(x) + RPI - 1 of
   // the tile; lane l fills row RIT(x) + l / CH, slot l % CH.
-  auto RIT = [&](int x) { return (8 * x + wave) * RPI; };
+  auto RIT = [&](int x) { return (NW * x + wave) * RPI; };
   const int drow = lane / CH;
   const int dchunk = (lane % CH) ^ swz(RIT(0) % 16 + drow);  // RIT(x) mod 16 is the same for all x
-  static_assert((8 * RPI) % 16 == 0, "load rows change the swizzle phase");
+  static_assert((NW * RPI) % 16 == 0, "load rows change the swizzle phase");
   const int kvoff = drow * (int)p.k_ss * (int)sizeof(T) + dchunk * 16;
   const int vvoff = drow * (int)p.v_ss * (int)sizeof(T) + dchunk * 16;
   // buffer resource of key tile t0 + t (zero bytes for tiles outside the
@@ -1173,6 +1201,18 @@ const void* pick_kernel(Dt dt, bool causal, bool varlen) {
   return varlen ? pick_kernel<D, false, true>(dt) : pick_kernel<D, false, false>(dt);
 }
 
+// compute units of the current device (cached per device)
+int compute_units() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDev && (n = cache[dev].load(std::memory_order_relaxed)) > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDev && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
@@ -1180,16 +1220,25 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   const void* fn = d == 64 ? pick_kernel<64>(dt, causal, varlen)
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
-  // fp16/bf16: 8-wave workgroups over pairs of query tiles
+  // fp16/bf16: units are pairs of query tiles, one 8-wave workgroup each at
+  // d = 128 and two 4-wave workgroups at d = 64
   const bool paired = dt != Dt::F32;
-  const long long grid =
+  const bool split = paired && d <= 64;
+  const long long units =
       varlen ? packed_units_per_head(p.total_q, p.b, paired ? 2 * kFwdBlockM : kFwdBlockM) * p.h
              : (long long)(paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
-  if (grid <= 0) return hipSuccess;
+  if (units <= 0) return hipSuccess;
+  const long long grid = split ? 2 * units : units;
+  if (grid > INT_MAX) return hipErrorInvalidValue;
   FwdParams arg = p;
+  if (split) {
+    const int cus = compute_units();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    arg.split_round = cus;
+  }
   void* args[] = {&arg};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(paired ? kFwdThreads16 : kFwdThreads),
-                         args, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid),
+                         dim3(paired ? fwd16_threads(d) : kFwdThreads), args, 0, stream);
 }
 
 }  // namespace sdpa07
