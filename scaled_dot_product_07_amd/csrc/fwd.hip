@@ -745,7 +745,9 @@ fwd16_kernel(FwdParams p) {
   float st_lse = 0.f;
   auto epi_stage = [&]() {
     const float l_tot = l_run + other_half(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // (the hardware reciprocal: within an ulp, far below the io type's
+    // rounding of O)
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
     typedef T t4 __attribute__((ext_vector_type(4)));
     st_row0 = row0;
     st_active = wave_active;
@@ -803,25 +805,46 @@ fwd16_kernel(FwdParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int sr = ln / CPR, sc = ln % CPR;
+      // all of the lane's chunks first, so that the stores wait once (row
+      // groups are RPS rows apart, so they share the chunk permutation)
+      static_assert(RPS % CPR == 0, "row groups keep the chunk permutation");
+      const int cofs = sr * D + (sc ^ (sr % CPR)) * 8;
+      i32x4 vrow[32 / RPS];
+#pragma unroll
+      for (int x = 0; x < 32 / RPS; ++x) vrow[x] = *(const i32x4*)&qbuf[x * RPS * D + cofs];
       // the stores carry the system-scope cache policy (sc0 sc1), which
       // writes the rows through to memory as they are stored; measured
       // faster than leaving them dirty in the L2 for the kernel's end. They
       // are buffer stores over the RPS rows of each instruction, whose
       // per-lane offsets fit 31 bits unless a row stride is beyond 2^26
-      // elements (then plain stores).
+      // elements (then plain stores); a wave whose 32 rows all exist, with
+      // a row stride below 2^24 elements, stores through one descriptor at
+      // its first row and a scalar offset per row group.
       const bool wt = p.o_ss < (1 << 26);
+      if (st_active && st_row0 + 32 <= q_len && p.o_ss < (1 << 24)) {
+        const T* base = Ob + (int64_t)max(st_row0, 0) * p.o_ss;
+        const auto rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kBufferFlags);
+        const int voff = (sr * (int)p.o_ss + sc * 8) * (int)sizeof(T);
 #pragma unroll
-      for (int x = 0; x < 32 / RPS; ++x) {
-        const int r = x * RPS + sr;
-        const i32x4 v = *(const i32x4*)&qbuf[r * D + (sc ^ (r % CPR)) * 8];
-        if (st_active && st_row0 + r < q_len) {
-          if (wt) {
-            const T* base = Ob + (int64_t)max(st_row0 + x * RPS, 0) * p.o_ss;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                v, __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kBufferFlags),
-                (sr * (int)p.o_ss + sc * 8) * (int)sizeof(T), 0, kCacheSystemScope);
-          } else {
-            *(i32x4*)(Ob + (int64_t)(st_row0 + r) * p.o_ss + sc * 8) = v;
+        for (int x = 0; x < 32 / RPS; ++x)
+          __builtin_amdgcn_raw_buffer_store_b128(vrow[x], rs, voff,
+                                                 x * RPS * (int)p.o_ss * (int)sizeof(T),
+                                                 kCacheSystemScope);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 32 / RPS; ++x) {
+          const int r = x * RPS + sr;
+          if (st_active && st_row0 + r < q_len) {
+            if (wt) {
+              const T* base = Ob + (int64_t)max(st_row0 + x * RPS, 0) * p.o_ss;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  vrow[x],
+                  __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kBufferFlags),
+                  (sr * (int)p.o_ss + sc * 8) * (int)sizeof(T), 0, kCacheSystemScope);
+            } else {
+              *(i32x4*)(Ob + (int64_t)(st_row0 + r) * p.o_ss + sc * 8) = vrow[x];
+            }
           }
         }
       }
