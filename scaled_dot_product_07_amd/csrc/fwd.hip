@@ -8,13 +8,15 @@
 //
 // fp16/bf16: query tiles of 128 rows go in pairs of one (b, h) or
 // (sequence, h) (for a causal band without a left bound heavy with light,
-// (n-1-i, i)), 32 rows per wave. At d = 128 one workgroup of 8 waves runs
-// both tiles of a pair: waves 0-3 hold the rows of the first, 4-7 those of
-// the second, so every SIMD hosts one wave of each. At d = 64 each tile has
-// a workgroup of its own (4 waves, 80 KB of LDS, two per CU), and the grid
-// puts the two tiles of a pair where the dispatcher places two workgroups
-// on one CU, so that they still share its SIMDs but not a barrier. Each
-// wave keeps, for its whole key range:
+// (n-1-i, i)), 32 rows per wave. At d = 64 and for causal bands each tile
+// has a workgroup of its own (4 waves; 80 KB of LDS at d = 64, 64 KB at
+// d = 128 where Q goes straight to registers; two per CU), and the grid puts
+// the two tiles of a pair where the dispatcher places two workgroups on one
+// CU, so that they share its SIMDs but not a barrier. Without a causal band
+// at d = 128 one workgroup of 8 waves runs both tiles of a pair over one key
+// stream: waves 0-3 hold the rows of the first, 4-7 those of the second, so
+// every SIMD hosts one wave of each. Each wave keeps, for its whole key
+// range:
 //   * its Q rows as MFMA B operands in VGPRs,
 //   * the fp32 output accumulator O^T (d x 32) in the MFMA C layout,
 //   * the offset m and running sum l of its rows.
@@ -118,10 +120,10 @@ using kPh = std::integral_constant<int, N>;
 constexpr float kTau = 8.f;
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(fwd16_threads(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd16_kernel(FwdParams p) {
+__global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
+    __attribute__((amdgpu_waves_per_eu(2, 2))) fwd16_kernel(FwdParams p) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
-  constexpr int NT = fwd16_threads(D);
+  constexpr int NT = fwd16_threads(D, CAUSAL);
   constexpr int NW = NT / 64;          // waves: 4 (one query tile) or 8 (two)
   constexpr bool SPLIT = NW == 4;
   // K and V tiles go from memory straight into LDS (buffer loads with the
@@ -147,7 +149,12 @@ fwd16_kernel(FwdParams p) {
   auto ring = [](int u) -> int { return (int)((unsigned)(u + NB) % (unsigned)NB); };
   constexpr int TILE = BN * D;         // elements per tile
   constexpr int QROWS = 32 * D;        // elements of one wave's Q rows
-  constexpr int LDS_ELEMS = 2 * NB * TILE + NW * QROWS;
+  // Q rows pass through LDS at d = 64 (whose epilogue reuses the area) and
+  // in the 8-wave workgroup (whole rows per load instruction); the one-tile
+  // d = 128 workgroup loads them straight into their registers, so that it
+  // needs only the ring (64 KB) and two fit on a CU
+  constexpr bool QLDS = D <= 64 || !SPLIT;
+  constexpr int LDS_ELEMS = 2 * NB * TILE + (QLDS ? NW * QROWS : 0);
   using M = Mfma16<T>;
   using v8 = typename M::v8;
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
@@ -731,7 +738,7 @@ fwd16_kernel(FwdParams p) {
   // chunks, so that each store instruction writes 8 complete rows. (At
   // d = 128 the kernel has no registers to spare for the exchange and keeps
   // the direct stores.)
-  T* const qbuf = lds + 2 * NB * TILE + wave * QROWS;
+  T* const qbuf = lds + (QLDS ? 2 * NB * TILE + wave * QROWS : 0);  // (d = 64 only)
   // The epilogue in two parts at d = 64: epi_stage normalises the rows into
   // the Q area and keeps the lane's statistic; epi_store reads the rows back
   // and stores them with the statistic. Rows finished in the middle of the
@@ -867,21 +874,31 @@ fwd16_kernel(FwdParams p) {
   // K(b+1+LK)): K(0 .. LK) and V(-1 .. LV-2) (V(-1), read by a first block's
   // no-op P.V, is all zeros). Only Q and K(0) have to land before the first
   // block; the steps' own waits cover the rest.
+  i32x4 qraw[D / 16];  // (Q straight to registers) the lane's chunks as loaded
   {
     const int rows = wave_active ? min(q_len - row0, 32) : 0;
     const T* qb = Q + (int64_t)max(row0, 0) * p.q_ss;
     const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)p.q_ss + D) * (int)sizeof(T);
-    const unsigned long long a = (unsigned long long)qb;
-    const i32x4 rq = {(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes,
-                      kBufferFlags};
-    // instruction x fills rows x * RPI + lane / CH of the wave's 32, each
-    // lane the global chunk that its slot holds under that row's swizzle
+    if constexpr (QLDS) {
+      const unsigned long long a = (unsigned long long)qb;
+      const i32x4 rq = {(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes,
+                        kBufferFlags};
+      // instruction x fills rows x * RPI + lane / CH of the wave's 32, each
+      // lane the global chunk that its slot holds under that row's swizzle
 #pragma unroll
-    for (int x = 0; x < 32 / RPI; ++x) {
-      const int qdchunk = (lane % CH) ^ swz((x * RPI + drow) % 16);
-      const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + qdchunk * 16;
-      dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T),
-          lds_at(2 * NB * TILE + wave * QROWS + x * RPI * D));
+      for (int x = 0; x < 32 / RPI; ++x) {
+        const int qdchunk = (lane % CH) ^ swz((x * RPI + drow) % 16);
+        const int qvoff = drow * (int)p.q_ss * (int)sizeof(T) + qdchunk * 16;
+        dma(rq, qvoff, x * RPI * (int)p.q_ss * (int)sizeof(T),
+            lds_at(2 * NB * TILE + wave * QROWS + x * RPI * D));
+      }
+    } else {
+      // lane: row col, chunks 2ks + hf (the B-operand layout below)
+      const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, bytes, kBufferFlags);
+      const int qvoff = col * (int)p.q_ss * (int)sizeof(T) + hf * 16;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        qraw[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qvoff, 32 * ks, 0));
     }
   }
   // the loads step b would have issued: V(b-1+LV) when it is a tile >= -1,
@@ -921,7 +938,10 @@ fwd16_kernel(FwdParams p) {
   const int qsign = __builtin_amdgcn_readfirstlane(p.negate_q ? (int)0x80008000 : 0);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    i32x4 raw = *(const i32x4*)&qbuf[col * D + (((2 * ks + hf) ^ sk) * 8)];
+    i32x4 raw;
+    if constexpr (QLDS) raw = *(const i32x4*)&lds[2 * NB * TILE + wave * QROWS + col * D +
+                                                   (((2 * ks + hf) ^ sk) * 8)];
+    else raw = qraw[ks];
     raw ^= qsign;
     qf[ks] = __builtin_bit_cast(v8, raw);
   }
@@ -1243,10 +1263,10 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   const void* fn = d == 64 ? pick_kernel<64>(dt, causal, varlen)
                            : pick_kernel<128>(dt, causal, varlen);
   if (!fn) return hipErrorInvalidValue;
-  // fp16/bf16: units are pairs of query tiles, one 8-wave workgroup each at
-  // d = 128 and two 4-wave workgroups at d = 64
+  // fp16/bf16: units are pairs of query tiles, two 4-wave workgroups each
+  // (d = 64, causal) or one 8-wave workgroup (non-causal d = 128)
   const bool paired = dt != Dt::F32;
-  const bool split = paired && d <= 64;
+  const bool split = paired && (d <= 64 || causal);
   const long long units =
       varlen ? packed_units_per_head(p.total_q, p.b, paired ? 2 * kFwdBlockM : kFwdBlockM) * p.h
              : (long long)(paired ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * p.b * p.h;
@@ -1261,7 +1281,7 @@ hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen
   }
   void* args[] = {&arg};
   return hipLaunchKernel(fn, dim3((unsigned)grid),
-                         dim3(paired ? fwd16_threads(d) : kFwdThreads), args, 0, stream);
+                         dim3(paired ? fwd16_threads(d, causal) : kFwdThreads), args, 0, stream);
 }
 
 }  // namespace sdpa07

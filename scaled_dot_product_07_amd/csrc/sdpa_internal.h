@@ -45,8 +45,8 @@ struct FwdParams {
   const float* scale_o;
   float* amax_o;
   float scale;
-  // fp16/bf16 forward at d <= 64: units per round of the one-tile grid (the
-  // device's compute-unit count; set by the launcher)
+  // fp16/bf16 forward: units per round of the one-tile grid (the device's
+  // compute-unit count; set by the launcher)
   int split_round;
 };
 
@@ -86,9 +86,14 @@ struct BwdParams {
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (32 per wave)
 constexpr int kFwdBlockN = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;    // fp32 forward workgroup
-constexpr int kFwdThreads16 = 512;  // fp16/bf16 forward workgroup at d = 128 (two query tiles)
-constexpr int kFwdThreads16s = 256;  // fp16/bf16 forward workgroup at d <= 64 (one query tile)
-constexpr int fwd16_threads(int d) { return d <= 64 ? kFwdThreads16s : kFwdThreads16; }
+// fp16/bf16 forward workgroup: 4 waves over one query tile at d = 64 and
+// for causal bands, 8 waves over a pair of tiles sharing one key stream for
+// non-causal d = 128
+constexpr int kFwdThreads16 = 256;
+constexpr int kFwdThreads16Pair = 512;
+constexpr int fwd16_threads(int d, bool causal) {
+  return d <= 64 || causal ? kFwdThreads16 : kFwdThreads16Pair;
+}
 
 // Workgroups per head of a packed (THD) launch whose units hold unit_rows
 // query rows of one sequence (a 128-row tile, or a pair of them): every split
