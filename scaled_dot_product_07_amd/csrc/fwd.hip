@@ -1244,7 +1244,8 @@ const void* pick_kernel(Dt dt, bool causal, bool varlen) {
   return varlen ? pick_kernel<D, false, true>(dt) : pick_kernel<D, false, false>(dt);
 }
 
-// compute units of the current device (cached per device)
+}  // namespace
+
 int compute_units() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -1255,8 +1256,6 @@ int compute_units() {
   if (dev < kMaxDev && n > 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
-
-}  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
                       hipStream_t stream) {

@@ -74,6 +74,83 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p) {
   return w;
 }
 
+// One query tile per workgroup, the two tiles of a pair on one CU: the grid
+// runs in rounds of 2R workgroups (R = p.split_round, the compute-unit
+// count); in a round, workgroup j < R takes the first tile of the round's
+// pair unit j and workgroup R + j its second, the two that the dispatcher
+// places on one CU when the round is resident. Pairs: (n-1-i, i) for a
+// causal band without a left bound (equal work), (2i, 2i+1) otherwise.
+// Dense: unit -> (pair, b*h). Packed: unit -> (live pair of a sequence,
+// head), heads innermost, pairs of all sequences heaviest first. A
+// workgroup without a tile (the missing second tile of an odd count, or a
+// unit past the last pair) gets q_len = 0.
+template <bool VARLEN, bool CAUSAL>
+__device__ __forceinline__ Unit decode_unit_paired(const FwdParams& p) {
+  const int n_units = gridDim.x / 2;
+  const int R = p.split_round;
+  const int r = blockIdx.x / (2 * R);
+  const int rem = min(R, n_units - r * R);  // units in this round
+  const int off = blockIdx.x - r * 2 * R;
+  const int half = off / rem;
+  const int unit = r * R + off % rem;
+  const bool heavy = CAUSAL && p.window_left < 0;
+  Unit w;
+  int pair, n_qt;
+  if constexpr (VARLEN) {
+    w.hi = unit % p.h;
+    const PackedUnit pu = packed_unit(unit / p.h, p.b, heavy, [&](int s) -> int2 {
+      const int lq = packed_len(p.cu_q, s, p.total_q);
+      const int np = (lq + 2 * kFwdBlockM - 1) / (2 * kFwdBlockM);
+      if (heavy) return int2{np, (lq + kFwdBlockM - 1) / kFwdBlockM};
+      return int2{np, max((packed_len(p.cu_kv, s, p.total_kv) + kFwdBlockN - 1) / kFwdBlockN, 1)};
+    });
+    if (pu.seq < 0) {
+      w.qt = 0;
+      w.q_len = 0;
+      return w;
+    }
+    const int bi = pu.seq;
+    const int q0 = min(max(p.cu_q[bi], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[bi + 1], 0), p.total_q);
+    const int k0 = min(max(p.cu_kv[bi], 0), p.total_kv);
+    const int k1 = min(max(p.cu_kv[bi + 1], 0), p.total_kv);
+    w.q_len = max(q1 - q0, 0);
+    w.kv_len = max(k1 - k0, 0);
+    w.q_off = (int64_t)q0 * p.q_ss + (int64_t)w.hi * p.q_sh;
+    w.o_off = (int64_t)q0 * p.o_ss + (int64_t)w.hi * p.o_sh;
+    w.k_off = (int64_t)k0 * p.k_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)k0 * p.v_ss + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
+    w.lse_off = (int64_t)q0 * p.h + w.hi;
+    w.lse_st = p.h;
+    pair = pu.j;
+    n_qt = (w.q_len + kFwdBlockM - 1) / kFwdBlockM;
+  } else {
+    const int nbh = p.b * p.h;
+    pair = unit / nbh;
+    const int bh = unit % nbh;
+    const int bi = bh / p.h;
+    w.hi = bh % p.h;
+    w.q_len = p.s_q;
+    w.kv_len = p.s_kv;
+    w.q_off = (int64_t)bi * p.q_sb + (int64_t)w.hi * p.q_sh;
+    w.o_off = (int64_t)bi * p.o_sb + (int64_t)w.hi * p.o_sh;
+    w.k_off = (int64_t)bi * p.k_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.k_sh;
+    w.v_off = (int64_t)bi * p.v_sb + (int64_t)(w.hi / (p.h / p.h_kv)) * p.v_sh;
+    w.lse_off = ((int64_t)bi * p.h + w.hi) * p.s_q;
+    w.lse_st = 1;
+    n_qt = p.n_qtiles;
+  }
+  const int first = heavy ? n_qt - 1 - pair : 2 * pair;
+  const int second0 = heavy ? pair : 2 * pair + 1;
+  const int second = (heavy ? second0 < first : second0 < n_qt) ? second0 : -1;
+  w.qt = half ? second : first;
+  if (w.qt < 0) {
+    w.qt = 0;
+    w.q_len = 0;
+  }
+  return w;
+}
+
 // Per-lane softmax state update for one tile of 32 scores held in s[2][16]
 // (already masked with -inf). Returns alpha, the factor for the old O.
 __device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], float c, float& m_run,

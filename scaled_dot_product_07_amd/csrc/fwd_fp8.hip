@@ -39,6 +39,7 @@
 // e4m3 (max 448), keeps 10 binades of smaller values in the normal range,
 // and the accumulator rescale stays rare.
 
+#include <limits.h>
 #include <math.h>
 
 #include "fwd_common.h"
@@ -117,7 +118,7 @@ fwd8_kernel(FwdParams p) {
   static_assert((NW * RPI) % 16 == 0, "load rows change the permutation phase");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][BN * D];
 
-  const Unit w = decode_unit<VARLEN, CAUSAL>(p);
+  const Unit w = decode_unit_paired<VARLEN, CAUSAL>(p);
   if (w.qt * BM >= w.q_len) return;
   const unsigned char* __restrict__ Q = (const unsigned char*)p.q + w.q_off;
   const unsigned char* __restrict__ K = (const unsigned char*)p.k + w.k_off;
@@ -351,10 +352,15 @@ hipError_t launch_fwd_fp8(const FwdParams& p, Dt out, int d, bool causal, bool v
         hipLaunchKernel((const void*)&zero_float_kernel, dim3(1), dim3(1), za, 0, stream);
     if (e != hipSuccess) return e;
   }
-  const long long grid = varlen ? packed_units_per_head(p.total_q, p.b, kFwdBlockM) * p.h
-                                : (long long)p.n_qtiles * p.b * p.h;
-  if (grid <= 0) return hipSuccess;
+  // pairs of query tiles, one workgroup per tile (see decode_unit_paired)
+  const long long units = varlen ? packed_units_per_head(p.total_q, p.b, 2 * kFwdBlockM) * p.h
+                                 : (long long)((p.n_qtiles + 1) / 2) * p.b * p.h;
+  if (units <= 0) return hipSuccess;
+  const long long grid = 2 * units;
+  if (grid > INT_MAX) return hipErrorInvalidValue;
   FwdParams arg = p;
+  arg.split_round = compute_units();
+  if (arg.split_round <= 0) return hipErrorInvalidDevice;
   void* args[] = {&arg};
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kF8Threads), args, 0, stream);
 }

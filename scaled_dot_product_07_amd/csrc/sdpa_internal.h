@@ -104,6 +104,9 @@ constexpr long long packed_units_per_head(long long total, long long num_seqs, i
 }
 
 // Enqueue the forward; returns the launch status.
+// compute units of the current device (cached per device; 0 on error)
+int compute_units();
+
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, bool varlen,
                       hipStream_t stream);
 
