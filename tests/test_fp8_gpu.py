@@ -48,6 +48,9 @@ CASES = [
     ("bf16", 2, 6, 1, 130, 330, 128, False, False, -1, 0.088, 1.0, 1.0, 1.0, 1.0),
     ("bf16", 1, 2, 2, 300, 500, 64, False, False, 70, 0.125, 1.0, 1.0, 1.0, 1.0),
     ("bf16", 1, 1, 1, 1, 1, 64, True, False, -1, 0.125, 1.0, 1.0, 1.0, 1.0),
+    # more tile pairs than compute units (rounds, a partial last one; 3 tiles
+    # per head leave one pair of each head without its second tile)
+    ("bf16", 1, 150, 150, 384, 384, 64, True, False, -1, 0.125, 1.0, 1.0, 1.0, 1.0),
 ]
 
 
