@@ -738,19 +738,27 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
   // chunks, so that each store instruction writes 8 complete rows. (At
   // d = 128 the kernel has no registers to spare for the exchange and keeps
   // the direct stores.)
-  T* const qbuf = lds + (QLDS ? 2 * NB * TILE + wave * QROWS : 0);  // (d = 64 only)
-  // The epilogue in two parts at d = 64: epi_stage normalises the rows into
-  // the Q area and keeps the lane's statistic; epi_store reads the rows back
-  // and stores them with the statistic. Rows finished in the middle of the
-  // key loop are stored only after its last step: a global store counts in
-  // vmcnt like the loads, so a store in flight would hold up the wave's next
-  // counted wait (and through the barrier the workgroup) until memory has
-  // acknowledged it. (At d = 128 the rows are stored at once.)
+  // where a wave stages its finished rows: its Q area (d = 64, and the
+  // 8-wave workgroup), else its quarter of the K ring, which no wave reads
+  // after the last step's barrier
+  T* const qbuf = lds + (QLDS ? 2 * NB * TILE + wave * QROWS : wave * QROWS);
+  static_assert(QLDS || NW * QROWS <= NB * TILE, "staging rows exceed the K ring");
+  // The epilogue in two parts: epi_stage normalises the rows into the
+  // staging area and keeps the lane's statistic; epi_store reads the rows
+  // back and stores them whole, with the statistic. At d = 64 rows finished
+  // in the middle of the key loop are stored only after its last step: a
+  // global store counts in vmcnt like the loads, so a store in flight would
+  // hold up the wave's next counted wait (and through the barrier the
+  // workgroup) until memory has acknowledged it. At d = 128 only the rows
+  // finished at the last step go through LDS; rows finished earlier (in the
+  // one-tile workgroup, whose staging area is its K ring, still in use) are
+  // stored at once from the accumulator layout.
   int st_row0 = 0;          // the staged rows: first row, any row, and the
   bool st_active = false;   // lane's row and statistic
   bool st_qvalid = false;
   float st_lse = 0.f;
-  auto epi_stage = [&]() {
+  auto epi_stage = [&](auto staged) {
+    constexpr bool STAGED = decltype(staged)::value;
     const float l_tot = l_run + other_half(l_run);
     // (the hardware reciprocal: within an ulp, far below the io type's
     // rounding of O)
@@ -760,7 +768,7 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
     st_active = wave_active;
     st_qvalid = q_valid;
     st_lse = l_tot > 0.f ? (m_cur + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if constexpr (D <= 64) {
+    if constexpr (STAGED) {
       constexpr int CPR = D / 8;  // 16-byte chunks per row
       // (the lane's offsets from a fresh copy of its index, so that each
       // inlined copy computes them where it runs instead of sharing ones
@@ -798,7 +806,7 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
     }
   };
   auto epi_store = [&]() {
-    if constexpr (D <= 64) {
+    {
       constexpr int CPR = D / 8;     // 16-byte chunks per row
       constexpr int RPS = 64 / CPR;  // rows per store instruction
       T* Ob = fresh_uniform(O);
@@ -812,13 +820,20 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int sr = ln / CPR, sc = ln % CPR;
-      // all of the lane's chunks first, so that the stores wait once (row
-      // groups are RPS rows apart, so they share the chunk permutation)
-      static_assert(RPS % CPR == 0, "row groups keep the chunk permutation");
-      const int cofs = sr * D + (sc ^ (sr % CPR)) * 8;
+      // all of the lane's chunks first, so that the stores wait once (at
+      // d = 64 row groups are RPS rows apart and share the chunk permutation)
       i32x4 vrow[32 / RPS];
+      if constexpr (RPS % CPR == 0) {
+        const int cofs = sr * D + (sc ^ (sr % CPR)) * 8;
 #pragma unroll
-      for (int x = 0; x < 32 / RPS; ++x) vrow[x] = *(const i32x4*)&qbuf[x * RPS * D + cofs];
+        for (int x = 0; x < 32 / RPS; ++x) vrow[x] = *(const i32x4*)&qbuf[x * RPS * D + cofs];
+      } else {
+#pragma unroll
+        for (int x = 0; x < 32 / RPS; ++x) {
+          const int r = x * RPS + sr;
+          vrow[x] = *(const i32x4*)&qbuf[r * D + (sc ^ (r % CPR)) * 8];
+        }
+      }
       // the stores carry the system-scope cache policy (sc0 sc1), which
       // writes the rows through to memory as they are stored; measured
       // faster than leaving them dirty in the L2 for the kernel's end. They
@@ -859,8 +874,12 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
     }
   };
   auto epilogue = [&]() {
-    epi_stage();
-    epi_store();
+    if constexpr (D <= 64) {
+      epi_stage(std::true_type{});
+      epi_store();
+    } else {
+      epi_stage(std::false_type{});
+    }
   };
 
   if (n_steps == 0) {
@@ -1064,9 +1083,16 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
       if (last_in_pa) pv_only(vb, pa);
       else pv_only(vb, pb);
     }
-    epi_stage();
-    if (now) epi_store();
-    else store_owed = true;
+    if constexpr (D <= 64) {
+      epi_stage(std::true_type{});
+      if (now) epi_store();
+      else store_owed = true;
+    } else if (now) {
+      epi_stage(std::true_type{});
+      epi_store();
+    } else {
+      epi_stage(std::false_type{});
+    }
   };
   // the first step after the wave's own (step ws1, or step 0 for a wave
   // without keys) brings its last V; it drains there, then only loads (kept
