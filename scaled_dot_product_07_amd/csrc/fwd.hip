@@ -749,10 +749,10 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
   // in the middle of the key loop are stored only after its last step: a
   // global store counts in vmcnt like the loads, so a store in flight would
   // hold up the wave's next counted wait (and through the barrier the
-  // workgroup) until memory has acknowledged it. At d = 128 only the rows
-  // finished at the last step go through LDS; rows finished earlier (in the
-  // one-tile workgroup, whose staging area is its K ring, still in use) are
-  // stored at once from the accumulator layout.
+  // workgroup) until memory has acknowledged it. At d = 128 a wave that
+  // finishes early keeps its rows in the accumulator (its last P.V done at
+  // once) and stages them only after the last barrier, since the one-tile
+  // workgroup stages in its K ring, in use until then.
   int st_row0 = 0;          // the staged rows: first row, any row, and the
   bool st_active = false;   // lane's row and statistic
   bool st_qvalid = false;
@@ -1091,7 +1091,7 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
       epi_stage(std::true_type{});
       epi_store();
     } else {
-      epi_stage(std::false_type{});
+      store_owed = true;  // normalised, staged and stored after the last barrier
     }
   };
   // the first step after the wave's own (step ws1, or step 0 for a wave
@@ -1108,7 +1108,10 @@ __global__ void __launch_bounds__(fwd16_threads(D, CAUSAL))
   wait_vm(WaitAll{});
   __builtin_amdgcn_s_barrier();
   if (ws1 == n_steps && ws1 > ws0) drain(true);
-  if (store_owed) epi_store();
+  if (store_owed) {
+    if constexpr (D > 64) epi_stage(std::true_type{});
+    epi_store();
+  }
 }
 
 // ---------------------------------------------------------------------------
