@@ -299,21 +299,62 @@ fwd8_kernel(FwdParams p) {
   const float l_tot = l_half + other_half(l_half);
   const float inv = l_tot > 0.f ? ofac / l_tot : 0.f;
   float amax = 0.f;
-  if (q_valid) {
-    TO* orow = O + (int64_t)qi * p.o_ss;
+  // The rows leave through LDS (free after the loop's last barrier): each
+  // lane writes its 4-column pieces into the wave's 32 rows, laid out
+  // [row][d] with the 16-byte chunks XOR-permuted by the row, then reads
+  // back whole chunks, so that each store instruction writes complete rows
+  // (with the system-scope cache policy, written through as stored); the
+  // descriptor's byte bound drops the rows past the sequence.
+  static_assert(NW * 32 * D * (int)sizeof(TO) <= (int)sizeof(lds), "staging rows exceed the LDS");
+  TO* const stg = (TO*)&lds[0][0][0] + wave * 32 * D;
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR;  // rows per store instruction
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        typename Out4<TO>::type ov;
+    for (int rq = 0; rq < 4; ++rq) {
+      typename Out4<TO>::type ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = acc[db][4 * rq + e] * inv;
-          amax = fmaxf(amax, fabsf(x));
-          ov[e] = (TO)x;
-        }
-        *(typename Out4<TO>::type*)(orow + 32 * db + 8 * rq + 4 * hf) = ov;
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[db][4 * rq + e] * inv;
+        if (q_valid) amax = fmaxf(amax, fabsf(x));
+        ov[e] = (TO)x;
       }
+      *(typename Out4<TO>::type*)&stg[col * D + ((4 * db + rq) ^ (col % CPR)) * 8 + 4 * hf] = ov;
+    }
+  // the wave reads back what its other lanes wrote (LDS operations of one
+  // wave complete in order; the fences keep the compiler's order and wait)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  {
+    const int sr = lane / CPR, sc = lane % CPR;
+    i32x4 vrow[32 / RPS];
+#pragma unroll
+    for (int x = 0; x < 32 / RPS; ++x) {
+      const int r = x * RPS + sr;
+      vrow[x] = *(const i32x4*)&stg[r * D + (sc ^ (r % CPR)) * 8];
+    }
+    const int rows = wave_active ? min(w.q_len - row0, 32) : 0;
+    if (p.o_ss < (1 << 24)) {
+      const TO* base = O + (int64_t)max(row0, 0) * p.o_ss;
+      const int bytes = rows <= 0 ? 0 : ((rows - 1) * (int)p.o_ss + D) * (int)sizeof(TO);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferFlags);
+      const int voff = (sr * (int)p.o_ss + sc * 8) * (int)sizeof(TO);
+#pragma unroll
+      for (int x = 0; x < 32 / RPS; ++x)
+        __builtin_amdgcn_raw_buffer_store_b128(vrow[x], rs, voff,
+                                               x * RPS * (int)p.o_ss * (int)sizeof(TO),
+                                               kCacheSystemScope);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 32 / RPS; ++x) {
+        const int r = x * RPS + sr;
+        if (r < rows) *(i32x4*)(O + (int64_t)(row0 + r) * p.o_ss + sc * 8) = vrow[x];
+      }
+    }
+  }
+  if (q_valid) {
     if (hf == 0 && p.lse)
       p.lse[w.lse_off + (int64_t)qi * w.lse_st] =
           l_tot > 0.f ? (m_off - kF8Lift + __log2f(l_tot)) * kLn2 : -INFINITY;
