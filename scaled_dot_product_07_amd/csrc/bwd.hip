@@ -545,8 +545,18 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
     }
   }
 
-  // store: lane owns key kj, d rows 32db + 8rq + 4hf + 0..3
-  if (kj < sq.kv_len) {
+  // store: lane owns key kj, d rows 32db + 8rq + 4hf + 0..3; the rows go
+  // whole through the wave's part of the P exchange (every wave is past the
+  // loops' last barrier)
+  const int64_t out_ss = kside ? p.dv_ss : p.dk_ss;
+  if (out_ss < (1 << 24)) {
+    static_assert(kDkdvThreads / 64 * 32 * D * (int)sizeof(T) <= (int)sizeof(pl),
+                  "staging rows exceed the P exchange");
+    T* dst0 = kside ? (T*)p.dv + sq.koff(p.dv_sb, p.dv_sh, p.dv_ss, hk) + (int64_t)key0 * p.dv_ss
+                    : (T*)p.dk + sq.koff(p.dk_sb, p.dk_sh, p.dk_ss, hk) + (int64_t)key0 * p.dk_ss;
+    store_rows_via_lds<T, D>((T*)&pl[0][0][0] + wave * 32 * D, acc, kside ? 1.f : p.scale, dst0,
+                             out_ss, sq.kv_len - key0, lane);
+  } else if (kj < sq.kv_len) {
     T* dst = kside ? (T*)p.dv + sq.koff(p.dv_sb, p.dv_sh, p.dv_ss, hk) + (int64_t)kj * p.dv_ss
                    : (T*)p.dk + sq.koff(p.dk_sb, p.dk_sh, p.dk_ss, hk) + (int64_t)kj * p.dk_ss;
     const float f = kside ? 1.f : p.scale;
@@ -759,7 +769,15 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
     __syncthreads();
   }
 
-  if (q_valid) {
+  // dQ rows whole through the wave's part of the K buffers (every wave is
+  // past the loop's last barrier)
+  if (p.dq_ss < (1 << 24)) {
+    static_assert(kBwdThreads / 64 * 32 * D * (int)sizeof(T) <= (int)sizeof(kl),
+                  "staging rows exceed the K buffers");
+    T* dq0 = (T*)p.dq + sq.qoff(p.dq_sb, p.dq_sh, p.dq_ss, hi) + (int64_t)max(row0, 0) * p.dq_ss;
+    store_rows_via_lds<T, D>((T*)&kl[0][0] + wave * 32 * D, dq, p.scale, dq0, p.dq_ss,
+                             sq.q_len - row0, lane);
+  } else if (q_valid) {
     T* dqp = (T*)p.dq + sq.qoff(p.dq_sb, p.dq_sh, p.dq_ss, hi) + (int64_t)qi * p.dq_ss;
     typedef T t4v __attribute__((ext_vector_type(4)));
 #pragma unroll

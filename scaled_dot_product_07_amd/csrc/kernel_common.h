@@ -239,5 +239,54 @@ __device__ __forceinline__ int packed_len(const int32_t* cu, int s, int total) {
   return max(b - a, 0);
 }
 
+// Stores the 32 x D tile that a wave holds in the C layout of a transposed
+// product (lane: row lane % 32; register 4 rq + e of block db: column
+// 32 db + 8 rq + 4 (lane / 32) + e), scaled by f, as whole rows: the pieces
+// go into the wave's LDS area stg ([32][D], 16-byte chunks XOR-permuted by
+// the row), each lane reads back whole chunks, and each store instruction
+// writes 64 / (D / 8) complete rows with the system-scope cache policy
+// (written through as stored). Rows from n_rows on are dropped by the
+// descriptor's byte bound. base: row 0; row_stride in elements, below 2^24
+// (the caller's check). The LDS area must be free for the wave's use.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows_via_lds(T* stg, const f32x16 (&x)[D / 32], float f,
+                                                   T* base, int64_t row_stride, int n_rows,
+                                                   int lane) {
+  typedef T t4 __attribute__((ext_vector_type(4)));
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR;  // rows per store instruction
+  const int cl = lane % 32, hl = lane / 32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      t4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (T)(x[db][4 * rq + e] * f);
+      *(t4*)&stg[cl * D + ((4 * db + rq) ^ (cl % CPR)) * 8 + 4 * hl] = ov;
+    }
+  // the wave reads back what its other lanes wrote (LDS operations of one
+  // wave complete in order; the fences keep the compiler's order and wait)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int sr = lane / CPR, sc = lane % CPR;
+  i32x4 v[32 / RPS];
+#pragma unroll
+  for (int xi = 0; xi < 32 / RPS; ++xi) {
+    const int r = xi * RPS + sr;
+    v[xi] = *(const i32x4*)&stg[r * D + (sc ^ (r % CPR)) * 8];
+  }
+  const int rows = min(max(n_rows, 0), 32);
+  const int bytes = rows == 0 ? 0 : ((rows - 1) * (int)row_stride + D) * (int)sizeof(T);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferFlags);
+  const int voff = (sr * (int)row_stride + sc * 8) * (int)sizeof(T);
+#pragma unroll
+  for (int xi = 0; xi < 32 / RPS; ++xi)
+    __builtin_amdgcn_raw_buffer_store_b128(v[xi], rs, voff,
+                                           xi * RPS * (int)row_stride * (int)sizeof(T),
+                                           kCacheSystemScope);
+}
+
 }  // namespace
 }  // namespace sdpa07
