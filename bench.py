@@ -473,7 +473,7 @@ def bench_other_workloads(torch, sdpa, W, dev, flush, trace=True):
         e["frac_of_fp8_mfma_peak"] = round(e["tflops"] / PEAK_FP8_TFLOPS, 4)
         out[f"fwd_fp8_b{c.b}h{c.h}s{c.s_q}d{c.d}_{layout}"] = e
         del q, k, v, o
-    # causal bf16 backward b4 h16 s2048 d128 (three kernels per call)
+    # causal bf16 backward b4 h16 s2048 d128 (two kernels per call)
     c = W.BWD_BF16_B4H16S2048D128
     q, k, v, do = (x.to(dev) for x in W.case_inputs(c))
     o, lse = sdpa.fwd(q, k, v, scale=c.scale, causal=True)

@@ -9,11 +9,15 @@
 // entry: the chain starts with the dO.O row dot product, then the main pass
 // and the dQ pass).
 //
-// Three kernels, in order on one stream, no atomics (bit-identical results
+// Two kernels, in order on one stream, no atomics (bit-identical results
 // run to run):
-//   bwd_pre   D = rowsum(dO * O) and LSE in base 2 (LSE * log2 e; +inf for a
-//             row without visible keys so that its P is 0), one pass over
-//             dO and O;
+//   bwd_dq    one wave per 32 queries: its Q and dO rows stay in VGPRs, and
+//             64-key tiles of K, V stream through LDS. Each lane first forms
+//             its query's D = rowsum(dO * O) from its dO row and the O row,
+//             and LSE in base 2 (LSE * log2 e; +inf for a row without
+//             visible keys so that its P is 0), and writes both to the
+//             workspace. Per tile: S^T = K Q^T and dP^T = V dO^T (the lane
+//             owns one query), dS^T in VGPRs, then dQ^T += K^T dS^T;
 //   bwd_dkdv  one wave per 32 keys of one K/V head: its K and V rows stay in
 //             VGPRs as MFMA B operands, and 64-query tiles of Q, dO (with
 //             their LSE and D) of every query head that reads this K/V head
@@ -21,11 +25,7 @@
 //             head group in registers. Per tile: S = Q K^T and dP = dO V^T
 //             (the lane owns one key column), P and dS in VGPRs, then
 //             dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
-//             through the transposing LDS read ds_read_b64_tr_b16;
-//   bwd_dq    one wave per 32 queries: its Q and dO rows stay in VGPRs, and
-//             64-key tiles of K, V stream through LDS. Per tile: S^T = K Q^T
-//             and dP^T = V dO^T (the lane owns one query), dS^T in VGPRs, then
-//             dQ^T += K^T dS^T.
+//             through the transposing LDS read ds_read_b64_tr_b16.
 // The contraction index of the second products is relabelled exactly as in
 // the forward (P, dS go from the MFMA C layout to B operands in registers).
 //
@@ -49,10 +49,6 @@ namespace sdpa07 {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPreThreads = 256;
-constexpr int kPreRows = 4;     // rows per lane group of the preprocess kernel
-// rows per block of the preprocess kernel: d / 8 lanes per row
-constexpr int pre_block_rows(int d) { return kPreThreads / (d / 8) * kPreRows; }
 constexpr int kBwdThreads = 256;
 constexpr int kDkdvThreads = 512;  // four wave pairs
 constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (32 per wave pair)
@@ -99,139 +95,6 @@ struct Seq {
   }
   static __device__ int st_step(const BwdParams& p) { return VARLEN ? p.h : 1; }
 };
-
-// ---------------------------------------------------------------------------
-// D = rowsum(dO * O) in fp32 and LSE in base 2 for every query row. A block
-// takes pre_block_rows(D) consecutive rows of one (b, h) (dense) or tokens of one
-// head (packed), so that its rows share their base offsets and a row's
-// address is one multiply; D/8 lanes per row, kPreRows rows per lane group,
-// all loads issued before the first product. Workspace row index: (b, h, s)
-// dense, token * h + head packed.
-template <typename T, int D, bool VARLEN>
-__global__ void __launch_bounds__(kPreThreads) bwd_pre_kernel(BwdParams p, float* lse2) {
-  constexpr int LPR = D / 8;  // lanes per row
-  constexpr int RPB = kPreThreads / LPR;
-  constexpr int kPreBlockRows = pre_block_rows(D);
-  static_assert(RPB * kPreRows == kPreBlockRows, "rows per block");
-  const int tid = threadIdx.x;
-  const int sub = tid % LPR;
-  // the block's (b, h) or head, and its first row within it
-  int rows, hi, row0;
-  int64_t ob, gb;
-  if constexpr (VARLEN) {
-    hi = blockIdx.x % p.h;
-    row0 = (int)(blockIdx.x / p.h) * kPreBlockRows;
-    rows = p.total_q;
-    ob = (int64_t)hi * p.o_sh;
-    gb = (int64_t)hi * p.do_sh;
-  } else {
-    const int nch = (p.s_q + kPreBlockRows - 1) / kPreBlockRows;
-    const int bh = blockIdx.x / nch;
-    row0 = (int)(blockIdx.x % nch) * kPreBlockRows;
-    hi = bh % p.h;
-    const int bi = bh / p.h;
-    rows = p.s_q;
-    ob = (int64_t)bi * p.o_sb + (int64_t)hi * p.o_sh;
-    gb = (int64_t)bi * p.do_sb + (int64_t)hi * p.do_sh;
-  }
-  typedef T t8 __attribute__((ext_vector_type(8)));
-  t8 ov[kPreRows], gv[kPreRows];
-#pragma unroll
-  for (int k = 0; k < kPreRows; ++k) {
-    const int si = row0 + k * RPB + tid / LPR;
-    ov[k] = t8{};
-    gv[k] = t8{};
-    if (si < rows) {
-      ov[k] = *(const t8*)((const T*)p.o + ob + (int64_t)si * p.o_ss + sub * 8);
-      gv[k] = *(const t8*)((const T*)p.dout + gb + (int64_t)si * p.do_ss + sub * 8);
-    }
-  }
-  const long long st0 = VARLEN ? hi : (long long)(blockIdx.x / ((p.s_q + kPreBlockRows - 1) /
-                                                                 kPreBlockRows)) * p.s_q;
-  const int st = VARLEN ? p.h : 1;
-#pragma unroll
-  for (int k = 0; k < kPreRows; ++k) {
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(to_f(ov[k][e]), to_f(gv[k][e]), acc);
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPR);
-    const int si = row0 + k * RPB + tid / LPR;
-    if (si < rows && sub == 0) {
-      const long long r = st0 + (long long)si * st;
-      p.delta[r] = acc;
-      const float l = p.lse[r];
-      lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
-    }
-  }
-}
-
-// The dK/dV pass's Q and dO tiles in LDS: rows of D elements, unpadded,
-// whose 16-byte chunks are permuted by an XOR of the row index (only r mod
-// 16 matters), so that both ways a tile is read hit distinct banks: the MFMA
-// row-operand reads (ds_read_b128, 16 rows per phase) and the transposing
-// reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes). No row padding
-// serves both: the first needs a row stride of an odd number of 16-byte
-// groups modulo 256 B, the second one of 64 B. Logical chunk c of row r
-// sits at chunk c ^ tile_swz<D>(r).
-template <int D>
-__device__ __forceinline__ int tile_swz(int r) {
-  return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
-}
-
-// Row-operand read: row r, logical chunk ch (8 elements), with s = tile_swz(r).
-template <typename T, int D>
-__device__ __forceinline__ typename Mfma16<T>::v8 read_row(const T* base, int r, int ch, int s) {
-  return *(const typename Mfma16<T>::v8*)&base[r * D + ((ch ^ s) << 3)];
-}
-
-// Transposing LDS read of an A operand: lane (16-group g, index i) receives
-// rows rbase + 4hf + 0..3 and + 8 .. 11 of column cbase + 16(g%2) + i
-// (row = rbase + 4hf + (i / 4); s0, s1: tile_swz of row and of row + 8).
-template <typename T, int D>
-__device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row, int colv, int s0,
-                                                          int s1) {
-  const T* a0 = base + row * D + (((colv >> 3) ^ s0) << 3) + (colv & 7);
-  const T* a1 = base + (row + 8) * D + (((colv >> 3) ^ s1) << 3) + (colv & 7);
-  const i16x4 lo =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
-  const i16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a1));
-  return __builtin_bit_cast(typename Mfma16<T>::v8,
-                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Packs 32 fp32 values held in a [2] x 16 MFMA C layout into 4 B operands
-// for a 64-deep contraction (element e of MFMA t: register 8(t%2)+e of block t/2).
-template <typename T>
-__device__ __forceinline__ void pack_b(const f32x16 (&x)[2], typename Mfma16<T>::v8 (&out)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    i32x4 pk;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const f32x2 v = {x[t / 2][8 * (t % 2) + 2 * e2], x[t / 2][8 * (t % 2) + 2 * e2 + 1]};
-      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
-    }
-    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
-  }
-}
-
-// The same for one 32-key block: 16 values into the 2 B operands of a
-// 32-deep contraction (element e of MFMA t: register 8t + e).
-template <typename T>
-__device__ __forceinline__ void pack_b1(const f32x16& x, typename Mfma16<T>::v8 (&out)[2]) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    i32x4 pk;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const f32x2 v = {x[8 * t + 2 * e2], x[8 * t + 2 * e2 + 1]};
-      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
-    }
-    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK/dV: a pair of waves owns 32 keys of one K/V head, and the workgroup's
@@ -576,7 +439,7 @@ bwd_dkdv_kernel(BwdParams p, const float* lse2) {
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
-bwd_dq_kernel(BwdParams p, const float* lse2) {
+bwd_dq_kernel(BwdParams p, float* lse2) {
   // K and V tiles go from memory straight into double-buffered LDS (buffer
   // loads with the LDS flag, no staging registers), in unpadded rows whose
   // 16-byte chunks carry the chunk swizzle: the row reads (S^T, dP^T) and
@@ -630,8 +493,6 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
   const T* V = (const T*)p.v + sq.koff(p.v_sb, p.v_sh, p.v_ss, hk);
   const float c = p.scale_log2;
   const int64_t si = sq.st0(p, hi) + (int64_t)qi * Seq<VARLEN>::st_step(p);
-  const float l2 = q_valid ? lse2[si] : INFINITY;
-  const float dl = q_valid ? p.delta[si] : 0.f;
 
   v8 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -643,6 +504,27 @@ bwd_dq_kernel(BwdParams p, const float* lse2) {
     }
     qf[ks] = __builtin_bit_cast(v8, a);
     gf[ks] = __builtin_bit_cast(v8, b);
+  }
+  // this lane's query: D = rowsum(dO * O) (the two lane halves hold
+  // alternate 8-column chunks of the row) and the statistic in base 2 (+inf
+  // for a row that sees no key, so that its P is 0); both also go to the
+  // workspace for the dK/dV pass, which runs after this one
+  float dpart = 0.f;
+  if (q_valid) {
+    const T* Orow = (const T*)p.o + sq.qoff(p.o_sb, p.o_sh, p.o_ss, hi) + (int64_t)qi * p.o_ss;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const v8 o8 = __builtin_bit_cast(v8, *(const i16x8*)(Orow + 16 * ks + 8 * hf));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf(to_f(o8[e]), to_f(gf[ks][e]), dpart);
+    }
+  }
+  const float dl = dpart + other_half(dpart);
+  const float lraw = q_valid ? p.lse[si] : -INFINITY;
+  const float l2 = lraw == -INFINITY ? INFINITY : lraw * kLog2e;
+  if (q_valid && hf == 0) {
+    p.delta[si] = dl;
+    lse2[si] = l2;
   }
   f32x16 dq[D / 32];
 #pragma unroll
@@ -853,19 +735,20 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
     }
     return hipSuccess;
   }
-  // the workspace: D for every query row (padded to 64), then LSE in base 2
+  // the workspace: D for every query row (padded to 64), then LSE in base 2,
+  // both written by the dQ pass for every query row it covers (all of them)
+  // and read by the dK/dV pass after it
   float* lse2 = p.delta + (n + 63) / 64 * 64;
-  if (n > 0) {
-    constexpr int BR = pre_block_rows(D);
-    const long long g = VARLEN ? (long long)p.h * ((p.total_q + BR - 1) / BR)
-                               : (long long)p.b * p.h * ((p.s_q + BR - 1) / BR);
-    void* args[] = {&arg, &lse2};
-    e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D, VARLEN>, dim3((unsigned)g),
-                        dim3(kPreThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
   // packed sequences with no queries (or no keys) still get their dK, dV
   // (or dQ) rows written as zeros by these two kernels
+  const long long gq = VARLEN ? packed_units_per_head(p.total_q, p.b, kDqRows) * p.h
+                              : (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
+  if (gq > 0) {
+    void* args[] = {&arg, &lse2};
+    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gq),
+                        dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   const long long gk =
       VARLEN ? packed_units_per_head(p.total_kv, p.b, kDkdvKeys) * p.h_kv
              : (long long)p.b * p.h_kv * ((p.s_kv + kDkdvKeys - 1) / kDkdvKeys);
@@ -873,14 +756,6 @@ hipError_t launch_typed(const BwdParams& p, hipStream_t stream) {
     void* args[] = {&arg, &lse2};
     e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gk),
                         dim3(kDkdvThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  const long long gq = VARLEN ? packed_units_per_head(p.total_q, p.b, kDqRows) * p.h
-                              : (long long)p.b * p.h * ((p.s_q + kDqRows - 1) / kDqRows);
-  if (gq > 0) {
-    void* args[] = {&arg, &lse2};
-    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, CAUSAL, VARLEN>, dim3((unsigned)gq),
-                        dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
