@@ -97,6 +97,74 @@ struct Seq {
 };
 
 // ---------------------------------------------------------------------------
+// The dK/dV pass's Q and dO tiles in LDS: rows of D elements, unpadded,
+// whose 16-byte chunks are permuted by an XOR of the row index (only r mod
+// 16 matters), so that both ways a tile is read hit distinct banks: the MFMA
+// row-operand reads (ds_read_b128, 16 rows per phase) and the transposing
+// reads (ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes). No row padding
+// serves both: the first needs a row stride of an odd number of 16-byte
+// groups modulo 256 B, the second one of 64 B. Logical chunk c of row r
+// sits at chunk c ^ tile_swz<D>(r).
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  return D <= 64 ? (((r >> 1) ^ (((r >> 1) & 1) << 2)) & 7) : ((r ^ ((r & 3) << 2)) & 15);
+}
+
+// Row-operand read: row r, logical chunk ch (8 elements), with s = tile_swz(r).
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma16<T>::v8 read_row(const T* base, int r, int ch, int s) {
+  return *(const typename Mfma16<T>::v8*)&base[r * D + ((ch ^ s) << 3)];
+}
+
+// Transposing LDS read of an A operand: lane (16-group g, index i) receives
+// rows rbase + 4hf + 0..3 and + 8 .. 11 of column cbase + 16(g%2) + i
+// (row = rbase + 4hf + (i / 4); s0, s1: tile_swz of row and of row + 8).
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma16<T>::v8 read_tr(const T* base, int row, int colv, int s0,
+                                                          int s1) {
+  const T* a0 = base + row * D + (((colv >> 3) ^ s0) << 3) + (colv & 7);
+  const T* a1 = base + (row + 8) * D + (((colv >> 3) ^ s1) << 3) + (colv & 7);
+  const i16x4 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a1));
+  return __builtin_bit_cast(typename Mfma16<T>::v8,
+                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Packs 32 fp32 values held in a [2] x 16 MFMA C layout into 4 B operands
+// for a 64-deep contraction (element e of MFMA t: register 8(t%2)+e of block t/2).
+template <typename T>
+__device__ __forceinline__ void pack_b(const f32x16 (&x)[2], typename Mfma16<T>::v8 (&out)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    i32x4 pk;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const f32x2 v = {x[t / 2][8 * (t % 2) + 2 * e2], x[t / 2][8 * (t % 2) + 2 * e2 + 1]};
+      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
+    }
+    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
+  }
+}
+
+// The same for one 32-key block: 16 values into the 2 B operands of a
+// 32-deep contraction (element e of MFMA t: register 8t + e).
+template <typename T>
+__device__ __forceinline__ void pack_b1(const f32x16& x, typename Mfma16<T>::v8 (&out)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    i32x4 pk;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const f32x2 v = {x[8 * t + 2 * e2], x[8 * t + 2 * e2 + 1]};
+      pk[e2] = __builtin_bit_cast(int, __builtin_convertvector(v, typename Pack2<T>::type));
+    }
+    out[t] = __builtin_bit_cast(typename Mfma16<T>::v8, pk);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dK/dV: a pair of waves owns 32 keys of one K/V head, and the workgroup's
 // four pairs own 128 consecutive keys. The first wave of a pair (K side)
 // keeps the K rows of its keys as MFMA B operands; per query tile it computes
