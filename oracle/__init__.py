@@ -220,6 +220,52 @@ def fwd_fp8(q8, k8, v8, scale: float, causal: bool, threads: int = 0, *, descale
     return o, lse, float(np.max(np.abs(o))) if o.size else 0.0
 
 
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 value (round to nearest, ties to the even code) of each
+    non-negative float64 in x; values past the largest finite one (448)
+    saturate to it. The value set is that of e4m3_decode over all 256 codes
+    (OCP FP8 E4M3: bias 7, three mantissa bits, subnormals below 2^-6)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(x < 0) or np.any(np.isnan(x)):
+        raise ValueError("e4m3_round takes non-negative finite values")
+    codes = np.arange(128, dtype=np.uint8)  # the non-negative codes
+    vals = e4m3_decode(codes)
+    ok = np.isfinite(vals)
+    vals, codes = vals[ok], codes[ok]
+    order = np.argsort(vals, kind="stable")
+    vals, codes = vals[order], codes[order]
+    xc = np.minimum(x, vals[-1])
+    hi = np.clip(np.searchsorted(vals, xc, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    dlo, dhi = xc - vals[lo], vals[hi] - xc
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    return np.where(pick_hi, vals[hi], vals[lo])
+
+
+def fwd_fp8_rounded_p(q8, k8, v8, scale: float, causal: bool, lift: float = 4.0) -> np.ndarray:
+    """The FP8 forward with P cast to e4m3 before the P.V product (cudnn-frontend
+    PR #554 merge log, the FP8 forward entry that casts P before BMM2), at the
+    plainest scale for that cast: each row's P_j = e4m3(2^(log2(e) * scale *
+    (s_j - max_j s_j) + lift)), so the row's largest P is 2^lift, and
+    O = sum_j P_j V_j / sum_j P_j with both sums over the same rounded P.
+    Dense q8 [b,h,s_q,d], k8/v8 [b,h,s_kv,d] e4m3 codes, scale > 0, top-left
+    causal band when causal; rows with no visible key are not supported."""
+    q, k, v = _fp8_inputs(q8, k8, v8, 1.0, 1.0, 1.0)
+    if not scale > 0:
+        raise ValueError("scale must be positive")
+    s = np.einsum("bhid,bhjd->bhij", q, k) * float(scale)
+    if causal:
+        sq, skv = s.shape[-2], s.shape[-1]
+        vis = np.arange(skv)[None, :] <= np.arange(sq)[:, None]
+        s = np.where(vis, s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("every row needs a visible key")
+    x = (s - m) * np.log2(np.e) + float(lift)
+    p = np.where(np.isfinite(x), e4m3_round(np.exp2(np.where(np.isfinite(x), x, 0.0))), 0.0)
+    return np.einsum("bhij,bhjd->bhid", p, v) / np.sum(p, axis=-1, keepdims=True)
+
+
 def fwd_fp8_varlen(q8, k8, v8, cu_q, cu_kv, scale: float, causal: bool, threads: int = 0, *,
                    descale_q=1.0, descale_k=1.0, descale_v=1.0, scale_o=1.0,
                    bottom_right: bool = False, window_left: int = -1):

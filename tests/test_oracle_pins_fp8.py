@@ -139,3 +139,76 @@ def test_fwd_fp8_varlen_equals_dense_per_sequence():
         np.testing.assert_array_equal(lse[cu_q[i]:cu_q[i + 1]], ld[0].T)
         peak = max(peak, ad)
     assert amax == peak
+
+
+# ---- e4m3_round and the rounded-P forward ------------------------------------
+
+def test_e4m3_round_fixes_every_value():
+    """Every finite non-negative E4M3 value rounds to itself."""
+    v = oracle.e4m3_decode(np.arange(128, dtype=np.uint8))
+    v = v[np.isfinite(v)]
+    assert np.array_equal(oracle.e4m3_round(v), v)
+
+
+def test_e4m3_round_ties_to_even_and_nearest():
+    """Midpoints of neighbouring values go to the even code; points just off a
+    midpoint go to the nearer value; past 448 the value saturates."""
+    codes = np.arange(127, dtype=np.uint8)  # 0x00 .. 0x7e: finite, non-negative
+    v = oracle.e4m3_decode(codes)
+    lo, hi = v[:-1], v[1:]
+    mid = (lo + hi) / 2
+    even_hi = (codes[1:] % 2) == 0
+    assert np.array_equal(oracle.e4m3_round(mid), np.where(even_hi, hi, lo))
+    eps = (hi - lo) * 1e-6
+    assert np.array_equal(oracle.e4m3_round(mid - eps), lo)
+    assert np.array_equal(oracle.e4m3_round(mid + eps), hi)
+    assert oracle.e4m3_round(np.array([1e4]))[0] == 448.0
+
+
+def test_e4m3_round_matches_torch_cast():
+    """Against torch's own float8_e4m3fn cast (round to nearest even) on random
+    values in the finite range, an implementation the oracle does not use."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(0, 448, 20000), rng.uniform(0, 2.0 ** -5, 20000),
+                        2.0 ** rng.uniform(-10, 8, 20000)])
+    x = x[x <= 448]
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    # float32 first: exact for these draws' rounding except in the last bits,
+    # which cannot move an e4m3 decision (3 mantissa bits)
+    assert np.array_equal(oracle.e4m3_round(x.astype(np.float32).astype(np.float64)), ref)
+
+
+def test_fwd_fp8_rounded_p_equals_exact_when_every_p_is_a_power_of_two():
+    """scale = ln 2 and integer scores: every P = 2^(s - max + 4) is an
+    integer power of two, which e4m3 holds exactly, so the rounded-P forward
+    is the exact FP8 forward."""
+    b, h, s, d = 1, 2, 40, 16
+    rng = np.random.default_rng(3)
+    q = np.zeros((b, h, s, d)); q[..., 0] = 1.0
+    k = np.zeros((b, h, s, d)); k[..., 0] = rng.integers(0, 6, (b, h, s))
+    v = rng.uniform(-2, 2, (b, h, s, d))
+    enc = lambda a: torch.from_numpy(a).to(torch.float32).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    q8, k8, v8 = enc(q), enc(k), enc(v)
+    for causal in (False, True):
+        o_r = oracle.fwd_fp8_rounded_p(q8, k8, v8, float(np.log(2.0)), causal)
+        o_e, _, _ = oracle.fwd_fp8(q8, k8, v8, float(np.log(2.0)), causal)
+        assert np.allclose(o_r, o_e, rtol=1e-12, atol=1e-12)
+
+
+def test_fwd_fp8_rounded_p_rounds():
+    """With scores that are not integer in log2 units the cast changes P: the
+    result moves off the exact forward, by at most the cast's relative error
+    (2^-4) times max |V|."""
+    b, h, s, d = 1, 2, 48, 32
+    rng = np.random.default_rng(5)
+    enc = lambda a: torch.from_numpy(a).to(torch.float32).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    q8 = enc(rng.uniform(0, 1, (b, h, s, d)))
+    k8 = enc(rng.uniform(0, 1, (b, h, s, d)))
+    v8 = enc(rng.uniform(-1, 1, (b, h, s, d)))
+    o_r = oracle.fwd_fp8_rounded_p(q8, k8, v8, 0.3, True)
+    o_e, _, _ = oracle.fwd_fp8(q8, k8, v8, 0.3, True)
+    diff = np.abs(o_r - o_e).max()
+    vmax = np.abs(oracle.e4m3_decode(v8)).max()
+    assert 0 < diff <= 2 * 2.0 ** -4 * vmax
