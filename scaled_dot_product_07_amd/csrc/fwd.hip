@@ -73,24 +73,24 @@ namespace {
 // ---------------------------------------------------------------------------
 // fp16 / bf16 io.
 //
-// A workgroup of 8 waves owns two 128-row query tiles A and B of one
-// (b|sequence, h): waves 0-3 hold the rows of A, waves 4-7 those of B, 32
-// rows each, so every SIMD hosts one wave of each tile. Causal attention
-// without a left bound pairs tiles (n-1-i, i): both start at key 0, so one
-// stream of key tiles serves both, and every pair holds the same causal work
-// (the wave of the short tile finishes early and leaves its SIMD to the
-// other, which then runs alone at nearly the same speed per tile). Other
-// masks pair adjacent tiles (2i, 2i+1), whose key ranges nearly coincide.
+// Query tiles of 128 rows go in pairs of one (b|sequence, h), 32 rows per
+// wave. Causal attention without a left bound pairs tiles (n-1-i, i): every
+// pair holds the same causal work. Other masks pair adjacent tiles (2i,
+// 2i+1), whose key ranges nearly coincide. A one-tile workgroup (4 waves;
+// d = 64 and causal bands) runs one tile of a pair, and the grid places the
+// pair's other tile on the same CU; the 8-wave workgroup (non-causal d = 128)
+// runs both, waves 0-3 on tile A and 4-7 on tile B, so every SIMD hosts one
+// wave of each, over one stream of key tiles that both start at key 0.
 //
 // Step s of the key loop loads one 64-key tile of K and V (each wave loads
-// an eighth of it) and runs one straight-line block per wave whose rows see
-// the tile (see `block`): the QK^T products of tile s+1, the P.V products of
-// tile s-1 and the softmax of tile s, with the wave's share of the loads of
-// later tiles spread over the block. A wave takes part in every step's
-// barrier and loads, but computes only over the steps its own rows reach;
-// when they end it drains its last P.V and stores its rows while the other
-// waves go on. No partial results are merged: each wave sees every key tile
-// of its rows.
+// its share of it: a quarter or an eighth) and runs one straight-line block
+// per wave whose rows see the tile (see `block`): the QK^T products of tile
+// s+1, the P.V products of tile s-1 and the softmax of tile s, with the
+// wave's share of the loads of later tiles spread over the block. A wave
+// takes part in every step's barrier and loads, but computes only over the
+// steps its own rows reach; when they end it drains its last P.V, and its
+// rows leave after the last step. No partial results are merged: each wave
+// sees every key tile of its rows.
 //
 // Softmax offsets are lazy: the offset m of a row (log2 units) changes only
 // when a tile's scores rise well above it, and O and l always share it, so
