@@ -11,6 +11,8 @@ test). Two checks per entry point:
     (inside the library as well), the stream would be idle when the calls
     return. Afterwards the side stream's results must equal the default
     stream's bit for bit.
+A third check captures every entry point in one HIP graph and replays it:
+each replay must equal the eager results bit for bit.
 """
 
 import pytest
@@ -93,3 +95,41 @@ def test_no_host_sync_and_caller_stream(gpu):
         if key in ("ws", "wsv"):
             continue
         assert torch.equal(got[key], ref[key]), f"{key} differs between the two streams"
+
+
+def test_graph_replay_matches_eager(gpu):
+    """Every entry point captured in one HIP graph (as a caller that replays a
+    step does) gives the eager results on every replay. Between replays the
+    outputs and workspaces are refilled with junk by ordinary eager work, so
+    a replay that skipped a write, or read what an earlier one left, shows."""
+    import scaled_dot_product_07_amd as sdpa
+    announce("launch discipline: graph capture, three replays against eager")
+    x = _inputs(gpu)
+    ref = _outputs(x)
+    _run_all(sdpa, x, ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    got = _outputs(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _run_all(sdpa, x, got, side)  # one eager pass on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _run_all(sdpa, x, got, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for key, t in got.items():
+            if t.dtype == torch.uint8:
+                t.fill_(255)
+            else:
+                t.fill_(float("nan") if rep % 2 == 0 else -3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ref:
+            if key in ("ws", "wsv"):
+                continue
+            assert torch.equal(got[key], ref[key]), f"replay {rep}: {key} differs from eager"
