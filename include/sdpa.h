@@ -224,7 +224,8 @@ size_t sdpa_bwd_workspace_size(int b, int h, int s_q, int d, sdpa_dtype dtype);
  *   workspace: device buffer of at least sdpa_bwd_workspace_size() bytes,
  *     256-byte aligned; its contents on entry are ignored.
  * Deterministic: no atomics; repeated calls give bit-identical gradients.
- * Three kernels on `stream`: rowsum(dO * O), a dK/dV pass, a dQ pass.
+ * Two kernels on `stream`: a dQ pass, which also forms rowsum(dO * O) and
+ * the base-2 statistic into the workspace, then a dK/dV pass that reads them.
  * Cited: cudnn-frontend PR #554 (dense backward, gradients in the inputs'
  * layouts, deterministic flag honoured); its merge log, the SM80 backward
  * TemplateParams entry (the chain starts with the dO.O row dot product).
